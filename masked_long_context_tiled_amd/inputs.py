@@ -1,0 +1,211 @@
+"""Seeded synthetic inputs shared by the CPU oracle tests, the GPU tests and the bench.
+
+This module holds no attention arithmetic. It only:
+  * names the mask kinds and carries their parameters (``MaskSpec``),
+  * draws the random tensors (Q, K, V, dO) and rounds them to bf16 bit patterns,
+  * draws the random structure the workloads need (document lengths for the
+    packed-sequence masks, the keep matrix of a uniform block-sparse mask),
+  * lists the workload configurations by name.
+
+Both sides consume the same bits: the oracle upcasts the bf16 patterns to fp64,
+the GPU path uploads them as bf16.
+
+Source for the mask names and the problem shape: "LongCA-bench: 长上下文注意力基准测试"
+(xllm-io paper-review blog), section 三 "注意力掩码模式" (the 12 static masks and the
+two dynamic block masks) and section 四 "实验设置" (bf16, head dim 128, GQA 64:8 and
+MHA 64:64, sequence length 1K-512K).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field, replace
+from typing import Optional, Tuple
+
+import numpy as np
+
+# Mask kinds, in the order of the C enum ``attn_mask_kind``.
+MASK_KINDS = (
+    "full",
+    "causal",
+    "full_document",
+    "causal_document",
+    "full_sliding_window",
+    "causal_sliding_window",
+    "shared_question",
+    "prefix_lm_causal",
+    "causal_blockwise",
+    "global_sliding",
+    "block_sparse",
+)
+
+
+@dataclass(frozen=True)
+class MaskSpec:
+    """A mask kind and its parameters (positions are 0-based, in one packed sequence).
+
+    window          sliding window width w (FULL/CAUSAL SLIDING WINDOW, GLOBAL SLIDING)
+    prefix_len      bidirectional prefix length (PREFIX LM CAUSAL)
+    question_len    shared question length (SHARED QUESTION)
+    answer_len      length of each answer (SHARED QUESTION)
+    n_answers       number of answers (SHARED QUESTION)
+    block_len       causal block length (CAUSAL BLOCKWISE)
+    final_block_len length of the final block that sees everything before it (CAUSAL BLOCKWISE)
+    global_len      number of global tokens at the start (GLOBAL SLIDING)
+    cu_seqlens      document boundaries, cu_seqlens[0] = 0, cu_seqlens[-1] = T (DOCUMENT masks)
+    sparse_block    block edge b of a uniform block-sparse mask (64 or 128)
+    """
+
+    kind: str
+    window: int = 0
+    prefix_len: int = 0
+    question_len: int = 0
+    answer_len: int = 0
+    n_answers: int = 0
+    block_len: int = 0
+    final_block_len: int = 0
+    global_len: int = 0
+    cu_seqlens: Tuple[int, ...] = field(default_factory=tuple)
+    sparse_block: int = 0
+
+    def __post_init__(self):
+        if self.kind not in MASK_KINDS:
+            raise ValueError(f"unknown mask kind {self.kind!r}")
+
+    @property
+    def kind_id(self) -> int:
+        return MASK_KINDS.index(self.kind)
+
+    def with_(self, **kw) -> "MaskSpec":
+        return replace(self, **kw)
+
+
+# ---------------------------------------------------------------------------
+# bf16 bit patterns
+# ---------------------------------------------------------------------------
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (round to nearest, ties to even); return uint16 bits."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    b = x.view(np.uint32).astype(np.uint64)
+    rounded = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
+    return rounded.astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns to float32 (exact)."""
+    bits = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    return bf16_bits_to_f32(bits).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Random tensors
+# ---------------------------------------------------------------------------
+
+def attention_inputs(seed: int, T: int, Hq: int, Hk: int, d: int = 128,
+                     with_do: bool = True) -> dict:
+    """Q [T][Hq][d], K/V [T][Hk][d], dO [T][Hq][d] as bf16 bit patterns (uint16).
+
+    Drawn i.i.d. N(0,1) in float32 from ``numpy.random.default_rng(seed)`` in the
+    order Q, K, V, dO, then rounded to bf16.
+    """
+    rng = np.random.default_rng(seed)
+    out = {}
+    out["q"] = f32_to_bf16_bits(rng.standard_normal((T, Hq, d), dtype=np.float32))
+    out["k"] = f32_to_bf16_bits(rng.standard_normal((T, Hk, d), dtype=np.float32))
+    out["v"] = f32_to_bf16_bits(rng.standard_normal((T, Hk, d), dtype=np.float32))
+    if with_do:
+        out["do"] = f32_to_bf16_bits(rng.standard_normal((T, Hq, d), dtype=np.float32))
+    return out
+
+
+def document_cu_seqlens(seed: int, total: int, lo: int = 512, hi: int = 8192) -> Tuple[int, ...]:
+    """Packed-sequence document boundaries.
+
+    Lengths are integers uniform on [lo, hi] (inclusive), drawn one after another
+    from ``default_rng(seed)`` until they cover ``total``; the last one is cut so the
+    lengths sum to exactly ``total``.
+    """
+    rng = np.random.default_rng(seed)
+    cu = [0]
+    while cu[-1] < total:
+        n = int(rng.integers(lo, hi + 1))
+        cu.append(min(total, cu[-1] + n))
+    return tuple(cu)
+
+
+def block_sparse_keep(seed: int, Hq: int, nqb: int, nkb: int) -> np.ndarray:
+    """Keep matrix uint8 [Hq][nqb][nkb] of a uniform block-sparse mask at 50% density.
+
+    For every (query head, query block) exactly floor(nkb/2) key blocks are kept
+    (at least one): the diagonal block r (when r < nkb) is always kept, the rest are
+    the smallest of i.i.d. uniform keys drawn from ``default_rng(seed)``.
+    """
+    rng = np.random.default_rng(seed)
+    keys = rng.random((Hq, nqb, nkb))
+    r = np.arange(min(nqb, nkb))
+    keys[:, r, r] = -1.0
+    n_keep = max(1, nkb // 2)
+    order = np.argsort(keys, axis=2, kind="stable")[:, :, :n_keep]
+    keep = np.zeros((Hq, nqb, nkb), dtype=np.uint8)
+    np.put_along_axis(keep, order, 1, axis=2)
+    return keep
+
+
+# ---------------------------------------------------------------------------
+# Workload configurations (mask shapes of the benchmark pages' workloads)
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    T: int
+    Hq: int
+    Hk: int
+    mask: MaskSpec
+    d: int = 128
+
+
+def workloads(seed: int = 0) -> dict:
+    """Named workloads. Document boundaries depend on ``seed``."""
+    cu32 = document_cu_seqlens(seed, 32768)
+    w = {}
+    w["tiny_causal"] = Workload("tiny_causal", 512, 4, 1, MaskSpec("causal"))
+    for hk in (8, 64):
+        tag = "gqa" if hk == 8 else "mha"
+        w[f"full_8k_{tag}"] = Workload(f"full_8k_{tag}", 8192, 64, hk, MaskSpec("full"))
+        w[f"causal_8k_{tag}"] = Workload(f"causal_8k_{tag}", 8192, 64, hk, MaskSpec("causal"))
+    w["full_document_32k"] = Workload("full_document_32k", 32768, 64, 8,
+                                      MaskSpec("full_document", cu_seqlens=cu32))
+    w["causal_document_32k"] = Workload("causal_document_32k", 32768, 64, 8,
+                                        MaskSpec("causal_document", cu_seqlens=cu32))
+    w["full_sliding_window_32k"] = Workload("full_sliding_window_32k", 32768, 64, 8,
+                                            MaskSpec("full_sliding_window", window=4096))
+    w["causal_sliding_window_32k"] = Workload("causal_sliding_window_32k", 32768, 64, 8,
+                                              MaskSpec("causal_sliding_window", window=4096))
+    w["shared_question_16k"] = Workload(
+        "shared_question_16k", 16384, 64, 8,
+        MaskSpec("shared_question", question_len=2048, answer_len=3584, n_answers=4))
+    w["prefix_lm_causal_16k"] = Workload("prefix_lm_causal_16k", 16384, 64, 8,
+                                         MaskSpec("prefix_lm_causal", prefix_len=4096))
+    w["causal_blockwise_16k"] = Workload(
+        "causal_blockwise_16k", 16384, 64, 8,
+        MaskSpec("causal_blockwise", block_len=1024, final_block_len=2048))
+    w["global_sliding_16k"] = Workload("global_sliding_16k", 16384, 64, 8,
+                                       MaskSpec("global_sliding", global_len=128, window=2048))
+    w["causal_128k"] = Workload("causal_128k", 131072, 64, 8, MaskSpec("causal"))
+    for b in (128, 64):
+        w[f"block_sparse_64k_b{b}"] = Workload(f"block_sparse_64k_b{b}", 65536, 64, 8,
+                                               MaskSpec("block_sparse", sparse_block=b))
+    return w
+
+
+def keep_for(workload: Workload, seed: int) -> Optional[np.ndarray]:
+    """The keep matrix for a block-sparse workload (None for other masks)."""
+    if workload.mask.kind != "block_sparse":
+        return None
+    b = workload.mask.sparse_block
+    nb = -(-workload.T // b)
+    return block_sparse_keep(seed, workload.Hq, nb, nb)
