@@ -1,0 +1,266 @@
+#!/usr/bin/env python3
+"""Throughput of the masked attention hot path on one MI355X (gfx950).
+
+One step = one pass of the whole path over one batch of synthetic inputs that are
+already resident in HBM:
+  column-interval descriptor (host) -> device copy -> tile index (classifier + lists)
+  -> attn_fwd -> attn_bwd_preprocess (D = rowsum(dO*O), dQ cleared) -> attn_bwd_main.
+The default workload is CAUSAL at T = 8192, 64 query heads sharing 8 KV heads, head
+dim 128, bf16 inputs N(0,1) from a seed.
+
+Effective FLOPs count only visible (query, key) pairs U (from the descriptor, or from
+the keep matrix for block-sparse masks): forward 4*d*Hq*U, backward 10*d*Hq*U.
+`value` is the effective TFLOP/s of whole steps (fwd + bwd work / step wall time).
+Per-kernel times come from HIP events on the stream the kernels run on.
+
+Prints one JSON line on stdout. Progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from masked_long_context_tiled_amd import attn  # noqa: E402
+from masked_long_context_tiled_amd.inputs import attention_inputs, keep_for, workloads  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0
+METRIC = "effective attn TFLOPs fwd/bwd, 8K GQA 64:8 hd128 bf16 per mask; % MFMA peak"
+KERNEL_SOURCES = ["fwd.hip", "bwd.hip", "index.hip", "common.h"]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "masked_long_context_tiled_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def visible_pairs(spec, T, desc, keep) -> int:
+    """U: visible pairs per head (mean over heads for block-sparse)."""
+    if spec.kind == "block_sparse":
+        b = spec.sparse_block
+        nb = keep.shape[1]
+        sizes = np.minimum(b, T - np.arange(nb) * b).astype(np.int64)
+        per_head = np.einsum("hqk,q,k->h", keep.astype(np.int64), sizes, sizes)
+        return int(per_head.sum()) // keep.shape[0], int(per_head.sum())
+    d = desc.astype(np.int64)
+    U = int(((d[:, 1] - d[:, 0]) + (d[:, 3] - d[:, 2])).sum())
+    return U, None
+
+
+def traffic_for(workload: str, kernel: str):
+    """HBM bytes per launch from committed counter runs, if they match the current kernels."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_hash") != kernel_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, x, keep, heads: int):
+    """Time the fp64 CPU oracle (forward + backward) on a bounded sample: `heads` query
+    heads of the same KV group, every row. Reported as effective TFLOP/s."""
+    from oracle.attention import attention_backward   # test infrastructure, timed here only
+    from oracle.masks import visible_count
+    from masked_long_context_tiled_amd.inputs import bf16_bits_to_f64
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max(i.get("num_threads", 1) for i in threadpool_info()) if threadpool_info() else os.cpu_count()
+    except Exception:
+        cores = os.cpu_count()
+    hs = list(range(min(heads, wl.Hq)))
+    q = bf16_bits_to_f64(x["q"][:, hs])
+    do = bf16_bits_to_f64(x["do"][:, hs])
+    G = wl.Hq // wl.Hk
+    g = hs[0] // G
+    k = bf16_bits_to_f64(x["k"][:, g:g + 1])
+    v = bf16_bits_to_f64(x["v"][:, g:g + 1])
+    sub_keep = None if keep is None else keep[hs]
+    t0 = time.perf_counter()
+    attention_backward(q, k, v, do, wl.mask, keep=sub_keep)
+    dt = time.perf_counter() - t0
+    U = sum(visible_count(wl.mask, wl.T, h, sub_keep) for h in range(len(hs)))
+    flops = 14.0 * wl.d * U
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{len(hs)} query heads x all {wl.T} rows of {wl.name}, fwd+bwd fp64, {dt:.1f} s",
+            "seconds": round(dt, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="causal_8k_gqa", choices=sorted(workloads(0)))
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-heads", type=int, default=2, help="query heads in the oracle timing sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--out", default=None, help="also append the JSON line to this file")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the per-GPU share of a sharded run is the 1-GPU workload).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    attn.lib()   # fail loudly if the HIP library is missing
+
+    wl = workloads(args.seed)[args.workload]
+    T, Hq, Hk, d, spec = wl.T, wl.Hq, wl.Hk, wl.d, wl.mask
+    log(f"workload {wl.name}: T={T} Hq={Hq} Hk={Hk} mask={spec.kind}")
+    x = attention_inputs(args.seed, T, Hq, Hk)
+    keep = keep_for(wl, args.seed)
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v, do = up(x["q"]), up(x["k"]), up(x["v"]), up(x["do"])
+    sparse = spec.kind == "block_sparse"
+    prob = attn.problem(T, Hq, Hk, spec.kind, spec.sparse_block if sparse else 0)
+    idx_bytes = attn.tile_index_size(prob)
+    index = torch.empty(idx_bytes, dtype=torch.uint8, device=dev)
+    desc_dev = torch.empty((T, 4), dtype=torch.int32, device=dev)
+    keep_dev = torch.from_numpy(keep).to(dev) if sparse else None
+    o = torch.empty((T, Hq, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((Hq, T), dtype=torch.float32, device=dev)
+    dq = torch.empty((T, Hq, d), dtype=torch.float32, device=dev)
+    dk = torch.empty((T, Hk, d), dtype=torch.float32, device=dev)
+    dv = torch.empty((T, Hk, d), dtype=torch.float32, device=dev)
+    ws_bytes = attn.bwd_workspace_size(prob)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+
+    desc_host = None if sparse else attn.mask_desc_build(spec, T)
+    U, U_all = visible_pairs(spec, T, desc_host, keep)
+    # block-sparse U differs per head: use the exact total over heads
+    fwd_flops = 4.0 * d * (U_all if U_all is not None else Hq * U)
+    bwd_flops = 2.5 * fwd_flops
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    times = {"index": [], "fwd": [], "bwd_pre": [], "bwd_main": []}
+
+    def step(record: bool):
+        if sparse:
+            ev[0].record(stream)
+            attn.block_index_build(prob, keep_dev.data_ptr(), index.data_ptr(), idx_bytes, sp)
+        else:
+            dh = attn.mask_desc_build(spec, T)                     # a1 (host)
+            desc_dev.copy_(torch.from_numpy(dh))                   # synchronous, 16 B per key
+            ev[0].record(stream)
+            attn.tile_index_build(prob, desc_dev.data_ptr(), index.data_ptr(), idx_bytes, sp)   # a2
+        ev[1].record(stream)
+        attn.fwd(prob, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                 0 if sparse else desc_dev.data_ptr(), index.data_ptr(), idx_bytes, 0, 0, sp)       # a3
+        ev[2].record(stream)
+        attn.bwd_preprocess(prob, o.data_ptr(), do.data_ptr(), dq.data_ptr(), ws.data_ptr(), ws_bytes, sp)  # a4
+        ev[3].record(stream)
+        attn.bwd_main(prob, q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                      dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), 0 if sparse else desc_dev.data_ptr(),
+                      index.data_ptr(), idx_bytes, ws.data_ptr(), ws_bytes, sp)                     # a5
+        ev[4].record(stream)
+        if record:
+            ev[4].synchronize()
+            times["index"].append(ev[0].elapsed_time(ev[1]))
+            times["fwd"].append(ev[1].elapsed_time(ev[2]))
+            times["bwd_pre"].append(ev[2].elapsed_time(ev[3]))
+            times["bwd_main"].append(ev[3].elapsed_time(ev[4]))
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps, synchronised on both sides
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(False)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = 1e3 * wall / args.steps
+
+    # per-kernel event times over a second pass of the same steps
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    med = {k: float(np.median(v)) for k, v in times.items()}
+    mean = {k: float(np.mean(v)) for k, v in times.items()}
+    t_bwd = med["bwd_pre"] + med["bwd_main"]
+    fwd_tf = fwd_flops / (med["fwd"] * 1e-3) / 1e12
+    bwd_tf = bwd_flops / (t_bwd * 1e-3) / 1e12
+    main_tf = bwd_flops / (mean["bwd_main"] * 1e-3) / 1e12
+    value = (fwd_flops + bwd_flops) / (ms_per_step * 1e-3) / 1e12
+    log(f"step {ms_per_step:.3f} ms | index {med['index']:.3f} fwd {med['fwd']:.3f} "
+        f"bwd_pre {med['bwd_pre']:.3f} bwd_main {med['bwd_main']:.3f} ms | fwd {fwd_tf:.1f} TF/s "
+        f"bwd {bwd_tf:.1f} TF/s")
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "mask": spec.kind, "T": T, "Hq": Hq, "Hk": Hk, "head_dim": d,
+                   "global_batch": 1, "seq_len": T, "parallelism": "none", "seed": args.seed},
+        "visible_pairs_per_head": U,
+        "fwd": {"ms": round(med["fwd"], 4), "tflops": round(fwd_tf, 2),
+                "frac_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4)},
+        "bwd": {"ms": round(t_bwd, 4), "tflops": round(bwd_tf, 2),
+                "frac_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
+                "preprocess_ms": round(med["bwd_pre"], 4), "main_ms": round(med["bwd_main"], 4)},
+        "index_build_ms": round(med["index"], 4),
+        "roofline": {"kernel": "bwd_kernel (attn_bwd_main)", "bound": "mfma",
+                     "achieved": round(main_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(main_tf / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_for(wl.name, "bwd_kernel"),
+                     "avg_launch_ms": round(mean["bwd_main"], 4),
+                     "flops_per_launch": bwd_flops},
+        "kernel_hash": kernel_hash(),
+    }
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle on {args.cpu_heads} heads")
+        rec["cpu_baseline"] = cpu_baseline(wl, x, keep, args.cpu_heads)
+    else:
+        rec["cpu_baseline"] = None
+    line = json.dumps(rec)
+    print(line, flush=True)
+    if args.out:
+        with open(args.out, "a") as f:
+            f.write(line + "\n")
+
+
+if __name__ == "__main__":
+    main()

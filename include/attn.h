@@ -1,0 +1,239 @@
+/*
+ * attn.h - C ABI of the masked long-context attention library (libattn.so, gfx950).
+ *
+ * The operator is bf16 masked softmax attention, forward and backward,
+ *     O = softmax(scale * Q K^T + mask) V,
+ * over grouped query heads (GQA: Hq query heads share Hk key/value heads in contiguous
+ * groups of G = Hq / Hk; MHA is G = 1) at head dimension 128, for the mask families
+ * benchmarked on "LongCA-bench: 长上下文注意力基准测试" (xllm-io paper-review blog):
+ *   - section 三 "注意力掩码模式": the regular masks (FULL, CAUSAL, FULL/CAUSAL DOCUMENT
+ *     over packed sequences, FULL/CAUSAL SLIDING WINDOW), the heterogeneous masks
+ *     (SHARED QUESTION, PREFIX LM CAUSAL, CAUSAL BLOCKWISE, GLOBAL SLIDING) and the
+ *     dynamic Uniform Block mask (block-sparse, fixed 64x64 or 128x128 blocks);
+ *   - section 三 "稀疏注意力内核": block size 64 and 128, GQA and MHA, forward and
+ *     backward (the capability matrix of the sparse kernels);
+ *   - section 四 "实验设置": bf16, head dim 128, GQA 64:8 and MHA 64:64, long sequences.
+ * The pages give names only; the exact visibility rule of every mask is stated at
+ * attn_mask_kind below.
+ *
+ * Layouts (all row-major, contiguous, batch 1, one packed sequence of length T):
+ *   Q, dO, O : bf16  [T][Hq][128]        K, V : bf16 [T][Hk][128]
+ *   LSE      : fp32  [Hq][T]  natural-log log-sum-exp of each query row's scaled scores
+ *   dQ       : fp32  [T][Hq][128]        dK, dV : fp32 [T][Hk][128]
+ *   desc     : int32 [T][4]  column-interval mask descriptor (attn_mask_desc_build)
+ *   keep     : uint8 [Hq][nb][nb], nb = ceil(T / b): block-sparse keep matrix
+ * Query head h uses key/value head h / G.
+ *
+ * Ownership and threading: the caller allocates and frees every buffer (inputs,
+ * outputs, the tile index and the workspace); the library allocates nothing and keeps
+ * no global state, so calls are reentrant. Device entry points are asynchronous on
+ * the given stream (a hipStream_t passed as void*, NULL = the null stream) and return
+ * after the launches are queued. All argument validation happens before any launch:
+ * an error status means nothing was launched. A launch failure reported by the HIP
+ * runtime is returned as ATTN_ERR_HIP. No C++ exception crosses this interface.
+ *
+ * Fully masked rows (possible only with a hand-built descriptor or keep matrix) get
+ * O = 0, LSE = -inf and zero gradients.
+ */
+#ifndef MLCT_ATTN_H
+#define MLCT_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum attn_status {
+    ATTN_OK = 0,
+    ATTN_ERR_INVALID_ARG = 1,  /* null pointer, bad size, Hq % Hk != 0, bad cu_seqlens, ... */
+    ATTN_ERR_UNSUPPORTED = 2,  /* head_dim != 128, group size G not a power of two <= 256, ... */
+    ATTN_ERR_WORKSPACE = 3,    /* workspace or index buffer smaller than the queried size */
+    ATTN_ERR_HIP = 4           /* the HIP runtime reported a launch error */
+} attn_status;
+
+/*
+ * Mask kinds. i = query position, j = key position, 0-based in the packed sequence.
+ * visible(i, j) is the rule each kind implements (the readings of the page's names):
+ *   FULL                     true
+ *   CAUSAL                   j <= i
+ *   FULL_DOCUMENT            doc(i) == doc(j)           doc from cu_seqlens
+ *   CAUSAL_DOCUMENT          doc(i) == doc(j) && j <= i
+ *   FULL_SLIDING_WINDOW      |i - j| < window
+ *   CAUSAL_SLIDING_WINDOW    0 <= i - j < window
+ *   SHARED_QUESTION          j <= i && (j < question_len || ans(i) == ans(j)),
+ *                            ans(x) = (x - question_len) / answer_len for x >= question_len
+ *   PREFIX_LM_CAUSAL         j < prefix_len || j <= i
+ *   CAUSAL_BLOCKWISE         j <= i && (i >= T - final_block_len || i / block_len == j / block_len)
+ *   GLOBAL_SLIDING           i < global_len || j < global_len || |i - j| < window
+ *   BLOCK_SPARSE             keep[h][i / b][j / b] != 0 (per query head h, b = sparse_block)
+ * Every kind except BLOCK_SPARSE is head-independent and has at most two visible row
+ * intervals per key column, which is what the descriptor stores.
+ */
+typedef enum attn_mask_kind {
+    ATTN_MASK_FULL = 0,
+    ATTN_MASK_CAUSAL = 1,
+    ATTN_MASK_FULL_DOCUMENT = 2,
+    ATTN_MASK_CAUSAL_DOCUMENT = 3,
+    ATTN_MASK_FULL_SLIDING_WINDOW = 4,
+    ATTN_MASK_CAUSAL_SLIDING_WINDOW = 5,
+    ATTN_MASK_SHARED_QUESTION = 6,
+    ATTN_MASK_PREFIX_LM_CAUSAL = 7,
+    ATTN_MASK_CAUSAL_BLOCKWISE = 8,
+    ATTN_MASK_GLOBAL_SLIDING = 9,
+    ATTN_MASK_BLOCK_SPARSE = 10
+} attn_mask_kind;
+
+/* Mask parameters; fields a kind does not use are ignored. */
+typedef struct attn_mask_params {
+    int32_t kind;             /* attn_mask_kind */
+    int32_t window;           /* sliding window width w >= 1 */
+    int32_t prefix_len;       /* PREFIX_LM_CAUSAL: 0 <= prefix_len <= T */
+    int32_t question_len;     /* SHARED_QUESTION: T == question_len + n_answers * answer_len */
+    int32_t answer_len;
+    int32_t n_answers;
+    int32_t block_len;        /* CAUSAL_BLOCKWISE: block_len >= 1, 0 <= final_block_len <= T */
+    int32_t final_block_len;
+    int32_t global_len;       /* GLOBAL_SLIDING: 0 <= global_len <= T, window >= 1 */
+    int32_t n_docs;           /* DOCUMENT kinds: number of documents >= 1 */
+    const int32_t* cu_seqlens;/* host pointer, n_docs + 1 strictly increasing entries, 0 .. T */
+} attn_mask_params;
+
+/* One attention problem. */
+typedef struct attn_problem {
+    int32_t T;                /* packed sequence length, 1 <= T <= 2^24 */
+    int32_t Hq;               /* query heads */
+    int32_t Hk;               /* key/value heads; G = Hq / Hk must be a power of two <= 256 */
+    int32_t head_dim;         /* must be 128 */
+    float scale;              /* softmax scale; <= 0 selects 1 / sqrt(head_dim) */
+    int32_t mask_kind;        /* attn_mask_kind */
+    int32_t sparse_block;     /* BLOCK_SPARSE only: 64 or 128 */
+} attn_problem;
+
+/* Human-readable name of a status code (static storage). */
+const char* attn_status_string(attn_status s);
+
+/*
+ * Column-interval mask descriptor (host, synchronous). For every key column j it
+ * writes desc[j] = {a0, b0, a1, b1}: the query rows that see key j are exactly
+ * [a0, b0) U [a1, b1), with 0 <= a0 <= b0 <= a1 <= b1 <= T (an empty interval has
+ * a == b). This is the column-wise mask representation that the pages credit to
+ * FlashMask (section 三 "密集注意力内核", section 四 "密集内核性能"), restricted to
+ * two intervals, which every non-sparse kind above needs at most.
+ *   p        : mask parameters (kind must not be BLOCK_SPARSE)
+ *   T        : sequence length
+ *   desc_out : host int32 [T][4], written entirely on success, untouched on error
+ */
+attn_status attn_mask_desc_build(const attn_mask_params* p, int32_t T, int32_t* desc_out);
+
+/*
+ * Tile index: per-tile classes (EMPTY / PARTIAL / FULL) and the lists of non-empty
+ * tiles the kernels walk, for the tile shapes the kernels use for this problem. EMPTY
+ * tiles are skipped, FULL tiles run without per-element mask work, PARTIAL tiles
+ * evaluate the interval descriptor per element. For BLOCK_SPARSE the same buffer holds
+ * the block index built from the keep matrix instead.
+ * attn_tile_index_size gives the bytes the caller must allocate (device memory,
+ * 256-byte aligned); the size depends only on the problem.
+ */
+attn_status attn_tile_index_size(const attn_problem* prob, size_t* bytes_out);
+
+/* Tile shapes (query positions x key positions) of the forward and backward kernels,
+ * as used in the tile index. Valid for every mask kind except BLOCK_SPARSE. */
+attn_status attn_query_tile_shape(const attn_problem* prob, int32_t* fwd_bm, int32_t* fwd_bn,
+                                  int32_t* bwd_bm, int32_t* bwd_bn);
+
+/* Byte offsets of the sections of a tile index (for inspection and tests):
+ *   fwd_cls   uint8 [nqt_f][nkt_f]        class per forward tile (0 EMPTY, 1 PARTIAL, 2 FULL)
+ *   fwd_ptr   int32 [nqt_f + 1]           CSR row pointers
+ *   fwd_ent   int32 [nnz]                 (key tile << 1) | is_full, ascending per row
+ *   fwd_order int32 [nqt_f]               query tiles by descending list length (launch order)
+ *   bwd_cls   uint8 [nqt_b][nkt_b], bwd_ptr int32 [nkt_b + 1],
+ *   bwd_ent   int32 [nnz]                 (query tile << 1) | is_full, ascending per column
+ *   bwd_order int32 [nkt_b]               key tiles by descending list length
+ * For BLOCK_SPARSE: fwd_ptr/fwd_ent are the CSR of keep over rows (h * nb + qb), entries
+ * kb; bwd_ptr/bwd_ent the CSC over columns (g * nb + kb), entries (h - g*G) * nb + qb;
+ * the cls and order sections are unused (offset 0). */
+typedef struct attn_index_layout {
+    int32_t nqt_f, nkt_f, nqt_b, nkt_b;
+    size_t fwd_cls, fwd_ptr, fwd_ent, fwd_order;
+    size_t bwd_cls, bwd_ptr, bwd_ent, bwd_order;
+    size_t total_bytes;
+} attn_index_layout;
+attn_status attn_tile_index_layout(const attn_problem* prob, attn_index_layout* out);
+
+/*
+ * Build the tile index on the device from a descriptor (any kind but BLOCK_SPARSE).
+ *   desc_dev  : device int32 [T][4] from attn_mask_desc_build
+ *   index_dev : device buffer of attn_tile_index_size bytes
+ */
+attn_status attn_tile_index_build(const attn_problem* prob, const int32_t* desc_dev,
+                                  void* index_dev, size_t index_bytes, void* stream);
+
+/*
+ * Build the block index on the device from a keep matrix (BLOCK_SPARSE only; the page's
+ * "Uniform Block" dynamic mask, section 三 "动态掩码").
+ *   keep_dev  : device uint8 [Hq][nb][nb], nb = ceil(T / sparse_block)
+ *   index_dev : device buffer of attn_tile_index_size bytes
+ */
+attn_status attn_block_index_build(const attn_problem* prob, const uint8_t* keep_dev,
+                                   void* index_dev, size_t index_bytes, void* stream);
+
+/* Workspace bytes of attn_fwd / attn_bwd (0 means no workspace is needed). */
+attn_status attn_fwd_workspace_size(const attn_problem* prob, size_t* bytes_out);
+attn_status attn_bwd_workspace_size(const attn_problem* prob, size_t* bytes_out);
+
+/*
+ * Forward: O = softmax(scale * Q K^T + mask) V and LSE.
+ *   q, k, v   : device bf16 inputs (layouts above)
+ *   o         : device bf16 output [T][Hq][128]
+ *   lse       : device fp32 output [Hq][T]
+ *   desc_dev  : device descriptor (NULL for BLOCK_SPARSE)
+ *   index_dev : tile / block index built for this problem
+ *   ws        : workspace of attn_fwd_workspace_size bytes (may be NULL if that is 0)
+ */
+attn_status attn_fwd(const attn_problem* prob, const void* q, const void* k, const void* v,
+                     void* o, float* lse, const int32_t* desc_dev,
+                     const void* index_dev, size_t index_bytes,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Backward: gradients of L with dL/dO = dout, given the forward's O and LSE.
+ * Equivalent to attn_bwd_preprocess followed by attn_bwd_main.
+ *   dq        : device fp32 [T][Hq][128], overwritten
+ *   dk, dv    : device fp32 [T][Hk][128], overwritten
+ *   ws        : workspace of attn_bwd_workspace_size bytes (holds D = rowsum(dO * O))
+ */
+attn_status attn_bwd(const attn_problem* prob, const void* q, const void* k, const void* v,
+                     const void* o, const float* lse, const void* dout,
+                     float* dq, float* dk, float* dv, const int32_t* desc_dev,
+                     const void* index_dev, size_t index_bytes,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Backward, first step: D[h][i] = sum_c dO[i][h][c] * O[i][h][c] into the workspace
+ * (fp32 [Hq][T]) and dq cleared to zero (attn_bwd_main accumulates into it).
+ */
+attn_status attn_bwd_preprocess(const attn_problem* prob, const void* o, const void* dout,
+                                float* dq, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Backward, second step: recompute P on the non-empty tiles and accumulate
+ * dV = P^T dO, dK = scale * dS^T Q (written once per key) and dQ += scale * dS K
+ * (added into dq), with dS = P * (dO V^T - D). Requires attn_bwd_preprocess on the
+ * same ws / dq first (stream order).
+ */
+attn_status attn_bwd_main(const attn_problem* prob, const void* q, const void* k, const void* v,
+                          const float* lse, const void* dout,
+                          float* dq, float* dk, float* dv, const int32_t* desc_dev,
+                          const void* index_dev, size_t index_bytes,
+                          const void* ws, size_t ws_bytes, void* stream);
+
+/* Optional cast of fp32 gradients to bf16 (round to nearest even): out[i] = bf16(in[i]). */
+attn_status attn_cast_bf16(const float* in, void* out, size_t n, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLCT_ATTN_H */

@@ -1,0 +1,385 @@
+// C-ABI entry points: argument validation, the host column-interval descriptor builder,
+// the tile-index layout and the launches. No allocation, no global state.
+#include <math.h>
+#include <string.h>
+
+#include "common.h"
+
+namespace mlct {
+
+static bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+attn_status validate_problem(const attn_problem* p, Problem* out) {
+    if (!p) return ATTN_ERR_INVALID_ARG;
+    if (p->T < 1 || p->T > (1 << 24) || p->Hq < 1 || p->Hk < 1) return ATTN_ERR_INVALID_ARG;
+    if (p->Hq % p->Hk != 0) return ATTN_ERR_INVALID_ARG;
+    if (p->mask_kind < ATTN_MASK_FULL || p->mask_kind > ATTN_MASK_BLOCK_SPARSE)
+        return ATTN_ERR_INVALID_ARG;
+    if (p->head_dim != HEAD_DIM) return ATTN_ERR_UNSUPPORTED;
+    if (!(p->scale == p->scale) || isinf(p->scale)) return ATTN_ERR_INVALID_ARG;
+    const int G = p->Hq / p->Hk;
+    if (!is_pow2(G) || G > ROWS_PER_WG) return ATTN_ERR_UNSUPPORTED;
+    Problem P{};
+    P.T = p->T;
+    P.Hq = p->Hq;
+    P.Hk = p->Hk;
+    P.G = G;
+    P.kind = p->mask_kind;
+    P.scale = p->scale > 0.f ? p->scale : 1.0f / sqrtf((float)HEAD_DIM);
+    P.sparse = p->mask_kind == ATTN_MASK_BLOCK_SPARSE;
+    if (P.sparse) {
+        if (p->sparse_block != 64 && p->sparse_block != 128) return ATTN_ERR_UNSUPPORTED;
+        P.sblock = p->sparse_block;
+        P.nb = (P.T + P.sblock - 1) / P.sblock;
+        // the keep matrix and the block lists are indexed with 32-bit integers
+        if ((size_t)P.Hq * P.nb * P.nb > (size_t)INT32_MAX) return ATTN_ERR_UNSUPPORTED;
+    } else {
+        P.fBM = ROWS_PER_WG / G;
+        P.fBN = FWD_BN;
+        P.bBM = ROWS_PER_WG / G;
+        P.bBN = BWD_BN;
+        P.nqt_f = (P.T + P.fBM - 1) / P.fBM;
+        P.nkt_f = (P.T + P.fBN - 1) / P.fBN;
+        P.nqt_b = (P.T + P.bBM - 1) / P.bBM;
+        P.nkt_b = (P.T + P.bBN - 1) / P.bBN;
+        if ((size_t)P.nqt_f * P.nkt_f > (size_t)INT32_MAX / 2) return ATTN_ERR_UNSUPPORTED;
+    }
+    if (out) *out = P;
+    return ATTN_OK;
+}
+
+IndexLayout index_layout(const Problem& P) {
+    IndexLayout L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off = align256(off + bytes);
+        return at;
+    };
+    if (!P.sparse) {
+        const size_t nf = (size_t)P.nqt_f * P.nkt_f, nb = (size_t)P.nqt_b * P.nkt_b;
+        L.fwd_cls = take(nf);
+        L.fwd_ptr = take(((size_t)P.nqt_f + 1) * 4);
+        L.fwd_ent = take(nf * 4);
+        L.fwd_order = take((size_t)P.nqt_f * 4);
+        L.bwd_cls = take(nb);
+        L.bwd_ptr = take(((size_t)P.nkt_b + 1) * 4);
+        L.bwd_ent = take(nb * 4);
+        L.bwd_order = take((size_t)P.nkt_b * 4);
+    } else {
+        const size_t rows = (size_t)P.Hq * P.nb, cols = (size_t)P.Hk * P.nb;
+        const size_t all = rows * P.nb;
+        L.fwd_ptr = take((rows + 1) * 4);
+        L.fwd_ent = take(all * 4);
+        L.bwd_ptr = take((cols + 1) * 4);
+        L.bwd_ent = take(all * 4);
+    }
+    L.total = align256(off);
+    return L;
+}
+
+// ---------------------------------------------------------------------------------
+// Column-interval descriptor: for key column j the visible query rows are
+// [a0, b0) U [a1, b1). Each case below restates the kind's rule from attn.h in
+// column form.
+// ---------------------------------------------------------------------------------
+static attn_status build_desc(const attn_mask_params* mp, int32_t T, int32_t* out) {
+    const int k = mp->kind;
+    auto put = [&](int j, int a0, int b0, int a1, int b1) {
+        if (a0 >= b0) { a0 = b0 = 0; }
+        if (a1 >= b1) { a1 = b1 = 0; }
+        if (a0 == b0 && a1 != b1) { a0 = a1; b0 = b1; a1 = b1 = 0; }
+        out[4 * j + 0] = a0;
+        out[4 * j + 1] = b0;
+        out[4 * j + 2] = a1;
+        out[4 * j + 3] = b1;
+    };
+    auto imin = [](long a, long b) { return (int)(a < b ? a : b); };
+    auto imax = [](long a, long b) { return (int)(a > b ? a : b); };
+    switch (k) {
+    case ATTN_MASK_FULL:
+        for (int j = 0; j < T; ++j) put(j, 0, T, 0, 0);
+        return ATTN_OK;
+    case ATTN_MASK_CAUSAL:
+        for (int j = 0; j < T; ++j) put(j, j, T, 0, 0);
+        return ATTN_OK;
+    case ATTN_MASK_FULL_DOCUMENT:
+    case ATTN_MASK_CAUSAL_DOCUMENT: {
+        const int n = mp->n_docs;
+        const int32_t* cu = mp->cu_seqlens;
+        for (int d = 0; d < n; ++d)
+            for (int j = cu[d]; j < cu[d + 1]; ++j)
+                put(j, k == ATTN_MASK_FULL_DOCUMENT ? cu[d] : j, cu[d + 1], 0, 0);
+        return ATTN_OK;
+    }
+    case ATTN_MASK_FULL_SLIDING_WINDOW: {
+        const long w = mp->window;
+        for (int j = 0; j < T; ++j) put(j, imax(0, j - w + 1), imin(T, j + w), 0, 0);
+        return ATTN_OK;
+    }
+    case ATTN_MASK_CAUSAL_SLIDING_WINDOW: {
+        const long w = mp->window;
+        for (int j = 0; j < T; ++j) put(j, j, imin(T, j + w), 0, 0);
+        return ATTN_OK;
+    }
+    case ATTN_MASK_SHARED_QUESTION: {
+        const long Qn = mp->question_len, A = mp->answer_len;
+        for (int j = 0; j < T; ++j) {
+            if (j < Qn) put(j, j, T, 0, 0);                       // question key: every later row
+            else put(j, j, imin(T, Qn + ((j - Qn) / A + 1) * A), 0, 0);  // rest of its answer
+        }
+        return ATTN_OK;
+    }
+    case ATTN_MASK_PREFIX_LM_CAUSAL: {
+        const long P = mp->prefix_len;
+        for (int j = 0; j < T; ++j) put(j, j < P ? 0 : j, T, 0, 0);
+        return ATTN_OK;
+    }
+    case ATTN_MASK_CAUSAL_BLOCKWISE: {
+        const long b = mp->block_len, F = (long)T - mp->final_block_len;
+        for (int j = 0; j < T; ++j) {
+            if (j >= F) { put(j, j, T, 0, 0); continue; }
+            const int bend = imin(T, (j / b + 1) * b);            // rows of j's own block
+            if (bend >= F) put(j, j, T, 0, 0);                    // touches the final block
+            else put(j, j, bend, (int)F, T);
+        }
+        return ATTN_OK;
+    }
+    case ATTN_MASK_GLOBAL_SLIDING: {
+        const long Gl = mp->global_len, w = mp->window;
+        for (int j = 0; j < T; ++j) {
+            if (j < Gl) { put(j, 0, T, 0, 0); continue; }          // global key: every row
+            const int lo = imax(0, j - w + 1), hi = imin(T, j + w);
+            if (lo <= Gl) put(j, 0, imax(hi, Gl), 0, 0);          // window meets the global rows
+            else put(j, 0, (int)Gl, lo, hi);
+        }
+        return ATTN_OK;
+    }
+    default:
+        return ATTN_ERR_INVALID_ARG;
+    }
+}
+
+static attn_status validate_mask(const attn_mask_params* mp, int32_t T) {
+    if (!mp || T < 1 || T > (1 << 24)) return ATTN_ERR_INVALID_ARG;
+    switch (mp->kind) {
+    case ATTN_MASK_FULL:
+    case ATTN_MASK_CAUSAL:
+        return ATTN_OK;
+    case ATTN_MASK_FULL_DOCUMENT:
+    case ATTN_MASK_CAUSAL_DOCUMENT: {
+        if (mp->n_docs < 1 || !mp->cu_seqlens) return ATTN_ERR_INVALID_ARG;
+        const int32_t* cu = mp->cu_seqlens;
+        if (cu[0] != 0 || cu[mp->n_docs] != T) return ATTN_ERR_INVALID_ARG;
+        for (int d = 0; d < mp->n_docs; ++d)
+            if (cu[d + 1] <= cu[d]) return ATTN_ERR_INVALID_ARG;
+        return ATTN_OK;
+    }
+    case ATTN_MASK_FULL_SLIDING_WINDOW:
+    case ATTN_MASK_CAUSAL_SLIDING_WINDOW:
+        return mp->window >= 1 ? ATTN_OK : ATTN_ERR_INVALID_ARG;
+    case ATTN_MASK_SHARED_QUESTION:
+        if (mp->question_len < 0 || mp->answer_len < 1 || mp->n_answers < 1) return ATTN_ERR_INVALID_ARG;
+        if ((long)mp->question_len + (long)mp->n_answers * mp->answer_len != T) return ATTN_ERR_INVALID_ARG;
+        return ATTN_OK;
+    case ATTN_MASK_PREFIX_LM_CAUSAL:
+        return (mp->prefix_len >= 0 && mp->prefix_len <= T) ? ATTN_OK : ATTN_ERR_INVALID_ARG;
+    case ATTN_MASK_CAUSAL_BLOCKWISE:
+        return (mp->block_len >= 1 && mp->final_block_len >= 0 && mp->final_block_len <= T)
+                   ? ATTN_OK : ATTN_ERR_INVALID_ARG;
+    case ATTN_MASK_GLOBAL_SLIDING:
+        return (mp->global_len >= 0 && mp->global_len <= T && mp->window >= 1) ? ATTN_OK
+                                                                                : ATTN_ERR_INVALID_ARG;
+    default:
+        return ATTN_ERR_INVALID_ARG;   // BLOCK_SPARSE has no descriptor; unknown kinds
+    }
+}
+
+static attn_status hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
+
+}  // namespace mlct
+
+using namespace mlct;
+
+extern "C" {
+
+const char* attn_status_string(attn_status s) {
+    switch (s) {
+    case ATTN_OK: return "ATTN_OK";
+    case ATTN_ERR_INVALID_ARG: return "ATTN_ERR_INVALID_ARG";
+    case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED";
+    case ATTN_ERR_WORKSPACE: return "ATTN_ERR_WORKSPACE";
+    case ATTN_ERR_HIP: return "ATTN_ERR_HIP";
+    default: return "ATTN_ERR_UNKNOWN";
+    }
+}
+
+attn_status attn_mask_desc_build(const attn_mask_params* p, int32_t T, int32_t* desc_out) {
+    if (!desc_out) return ATTN_ERR_INVALID_ARG;
+    attn_status st = validate_mask(p, T);
+    if (st != ATTN_OK) return st;
+    return build_desc(p, T, desc_out);
+}
+
+attn_status attn_tile_index_size(const attn_problem* prob, size_t* bytes_out) {
+    Problem P;
+    attn_status st = validate_problem(prob, &P);
+    if (st != ATTN_OK) return st;
+    if (!bytes_out) return ATTN_ERR_INVALID_ARG;
+    *bytes_out = index_layout(P).total;
+    return ATTN_OK;
+}
+
+attn_status attn_query_tile_shape(const attn_problem* prob, int32_t* fwd_bm, int32_t* fwd_bn,
+                                  int32_t* bwd_bm, int32_t* bwd_bn) {
+    Problem P;
+    attn_status st = validate_problem(prob, &P);
+    if (st != ATTN_OK) return st;
+    if (P.sparse) return ATTN_ERR_INVALID_ARG;
+    if (!fwd_bm || !fwd_bn || !bwd_bm || !bwd_bn) return ATTN_ERR_INVALID_ARG;
+    *fwd_bm = P.fBM;
+    *fwd_bn = P.fBN;
+    *bwd_bm = P.bBM;
+    *bwd_bn = P.bBN;
+    return ATTN_OK;
+}
+
+attn_status attn_tile_index_layout(const attn_problem* prob, attn_index_layout* out) {
+    Problem P;
+    attn_status st = validate_problem(prob, &P);
+    if (st != ATTN_OK) return st;
+    if (!out) return ATTN_ERR_INVALID_ARG;
+    IndexLayout L = index_layout(P);
+    if (P.sparse) {
+        out->nqt_f = P.Hq * P.nb;
+        out->nkt_f = P.nb;
+        out->nqt_b = P.Hk * P.nb;
+        out->nkt_b = P.nb;
+    } else {
+        out->nqt_f = P.nqt_f;
+        out->nkt_f = P.nkt_f;
+        out->nqt_b = P.nqt_b;
+        out->nkt_b = P.nkt_b;
+    }
+    out->fwd_cls = L.fwd_cls;
+    out->fwd_ptr = L.fwd_ptr;
+    out->fwd_ent = L.fwd_ent;
+    out->fwd_order = L.fwd_order;
+    out->bwd_cls = L.bwd_cls;
+    out->bwd_ptr = L.bwd_ptr;
+    out->bwd_ent = L.bwd_ent;
+    out->bwd_order = L.bwd_order;
+    out->total_bytes = L.total;
+    return ATTN_OK;
+}
+
+attn_status attn_tile_index_build(const attn_problem* prob, const int32_t* desc_dev, void* index_dev,
+                                  size_t index_bytes, void* stream) {
+    Problem P;
+    attn_status st = validate_problem(prob, &P);
+    if (st != ATTN_OK) return st;
+    if (P.sparse || !desc_dev || !index_dev) return ATTN_ERR_INVALID_ARG;
+    if (index_bytes < index_layout(P).total) return ATTN_ERR_WORKSPACE;
+    return hip_status(launch_index_dense(P, reinterpret_cast<const int4*>(desc_dev), index_dev,
+                                         (hipStream_t)stream));
+}
+
+attn_status attn_block_index_build(const attn_problem* prob, const uint8_t* keep_dev, void* index_dev,
+                                   size_t index_bytes, void* stream) {
+    Problem P;
+    attn_status st = validate_problem(prob, &P);
+    if (st != ATTN_OK) return st;
+    if (!P.sparse || !keep_dev || !index_dev) return ATTN_ERR_INVALID_ARG;
+    if (index_bytes < index_layout(P).total) return ATTN_ERR_WORKSPACE;
+    return hip_status(launch_index_sparse(P, keep_dev, index_dev, (hipStream_t)stream));
+}
+
+attn_status attn_fwd_workspace_size(const attn_problem* prob, size_t* bytes_out) {
+    attn_status st = validate_problem(prob, nullptr);
+    if (st != ATTN_OK) return st;
+    if (!bytes_out) return ATTN_ERR_INVALID_ARG;
+    *bytes_out = 0;
+    return ATTN_OK;
+}
+
+attn_status attn_bwd_workspace_size(const attn_problem* prob, size_t* bytes_out) {
+    Problem P;
+    attn_status st = validate_problem(prob, &P);
+    if (st != ATTN_OK) return st;
+    if (!bytes_out) return ATTN_ERR_INVALID_ARG;
+    *bytes_out = align256((size_t)P.Hq * P.T * sizeof(float));   // D = rowsum(dO * O), [Hq][T]
+    return ATTN_OK;
+}
+
+attn_status attn_fwd(const attn_problem* prob, const void* q, const void* k, const void* v, void* o,
+                     float* lse, const int32_t* desc_dev, const void* index_dev, size_t index_bytes,
+                     void* ws, size_t ws_bytes, void* stream) {
+    (void)ws;
+    (void)ws_bytes;
+    Problem P;
+    attn_status st = validate_problem(prob, &P);
+    if (st != ATTN_OK) return st;
+    if (!q || !k || !v || !o || !lse || !index_dev) return ATTN_ERR_INVALID_ARG;
+    if (!P.sparse && !desc_dev) return ATTN_ERR_INVALID_ARG;
+    if (index_bytes < index_layout(P).total) return ATTN_ERR_WORKSPACE;
+    return hip_status(launch_fwd(P, q, k, v, o, lse, reinterpret_cast<const int4*>(desc_dev), index_dev,
+                                 (hipStream_t)stream));
+}
+
+static attn_status check_bwd_ws(const attn_problem* prob, const void* ws, size_t ws_bytes) {
+    size_t need = 0;
+    attn_bwd_workspace_size(prob, &need);
+    return (!ws || ws_bytes < need) ? ATTN_ERR_WORKSPACE : ATTN_OK;
+}
+
+attn_status attn_bwd_preprocess(const attn_problem* prob, const void* o, const void* dout, float* dq, void* ws,
+                                size_t ws_bytes, void* stream) {
+    Problem P;
+    attn_status st = validate_problem(prob, &P);
+    if (st != ATTN_OK) return st;
+    if (!o || !dout || !dq) return ATTN_ERR_INVALID_ARG;
+    if ((st = check_bwd_ws(prob, ws, ws_bytes)) != ATTN_OK) return st;
+    return hip_status(launch_bwd_pre(P, o, dout, dq, (float*)ws, (hipStream_t)stream));
+}
+
+attn_status attn_bwd_main(const attn_problem* prob, const void* q, const void* k, const void* v,
+                          const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                          const int32_t* desc_dev, const void* index_dev, size_t index_bytes, const void* ws,
+                          size_t ws_bytes, void* stream) {
+    Problem P;
+    attn_status st = validate_problem(prob, &P);
+    if (st != ATTN_OK) return st;
+    if (!q || !k || !v || !lse || !dout || !dq || !dk || !dv || !index_dev) return ATTN_ERR_INVALID_ARG;
+    if (!P.sparse && !desc_dev) return ATTN_ERR_INVALID_ARG;
+    if (index_bytes < index_layout(P).total) return ATTN_ERR_WORKSPACE;
+    if ((st = check_bwd_ws(prob, ws, ws_bytes)) != ATTN_OK) return st;
+    return hip_status(launch_bwd_main(P, q, k, v, lse, dout, dq, dk, dv, reinterpret_cast<const int4*>(desc_dev),
+                                      index_dev, (const float*)ws, (hipStream_t)stream));
+}
+
+attn_status attn_bwd(const attn_problem* prob, const void* q, const void* k, const void* v, const void* o,
+                     const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                     const int32_t* desc_dev, const void* index_dev, size_t index_bytes, void* ws,
+                     size_t ws_bytes, void* stream) {
+    Problem P;
+    attn_status st = validate_problem(prob, &P);
+    if (st != ATTN_OK) return st;
+    // validate everything before the first launch
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv || !index_dev)
+        return ATTN_ERR_INVALID_ARG;
+    if (!P.sparse && !desc_dev) return ATTN_ERR_INVALID_ARG;
+    if (index_bytes < index_layout(P).total) return ATTN_ERR_WORKSPACE;
+    if ((st = check_bwd_ws(prob, ws, ws_bytes)) != ATTN_OK) return st;
+    st = attn_bwd_preprocess(prob, o, dout, dq, ws, ws_bytes, stream);
+    if (st != ATTN_OK) return st;
+    return attn_bwd_main(prob, q, k, v, lse, dout, dq, dk, dv, desc_dev, index_dev, index_bytes, ws, ws_bytes,
+                         stream);
+}
+
+attn_status attn_cast_bf16(const float* in, void* out, size_t n, void* stream) {
+    if (n == 0) return ATTN_OK;
+    if (!in || !out) return ATTN_ERR_INVALID_ARG;
+    return hip_status(launch_cast_bf16(in, out, n, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,299 @@
+// Masked attention forward for gfx950.
+//
+// Work item = one workgroup = 32 * NW (head, position) rows that walk the same list of
+// 64-key tiles. Dense masks: the rows are the G query heads of one KV head times
+// 256/G consecutive positions (one query tile of the tile index), so every K/V tile
+// staged in LDS is reused by the whole GQA group. Block-sparse: the rows are one
+// (query head, query block) row of the keep matrix.
+//
+// Each wave owns 32 rows and computes the transposed scores S^T = K Q^T with
+// v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = Q held in registers), so a lane holds
+// one query row and 16 keys per 32-key block: the row max and row sum are mostly
+// in-lane, with one exchange between the two wave halves. The probabilities P^T then
+// feed O^T += V^T P^T directly as the B operand (no register shuffles); V is stored
+// transposed in LDS for the A operand.
+//
+// Per tile: EMPTY tiles are not in the list; FULL tiles skip all mask work; PARTIAL
+// tiles (and the ragged last tile) test each element against the key's two visible row
+// intervals. Online softmax runs in base 2 with a lazy rescale: the running max used
+// for the exponent is only raised when a row's new max exceeds it by more than 8
+// (so P <= 2^8), which keeps the O rescale off the common path; O / l and
+// LSE = (m + log2 l) * ln 2 are exact whatever max was used.
+#include "common.h"
+
+namespace mlct {
+
+constexpr int KS_LD = HEAD_DIM + 8;   // bf16 per K row in LDS (pad against bank conflicts)
+constexpr int VT_LD = FWD_BN + 4;     // bf16 per V^T row in LDS
+constexpr float RESCALE_SLACK = 8.0f; // log2 units the running max may lag behind
+
+struct FwdArgs {
+    const bf16* q;
+    const bf16* k;
+    const bf16* v;
+    bf16* o;
+    float* lse;
+    const int4* desc;
+    const int* ptr;
+    const int* ent;
+    const int* order;
+    int T, Hq, Hk, G, BMq, nb, sblock;
+    float c;   // scale * log2(e)
+};
+
+template <int NW, bool SPARSE>
+__global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
+    constexpr int NT = NW * 64;
+    constexpr int KCH = 1024 / NT;   // 16-byte K chunks per thread per tile
+    constexpr int VUN = 512 / NT;    // (key pair, 8 dims) V units per thread per tile
+    constexpr int TPE = SPARSE ? NW / 2 : 1;   // 64-key tiles per list entry
+
+    __shared__ __attribute__((aligned(16))) bf16 Ks[FWD_BN * KS_LD];
+    __shared__ __attribute__((aligned(16))) bf16 Vt[HEAD_DIM * VT_LD];
+    __shared__ int4 Ds[FWD_BN];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int l32 = lane & 31, hf = lane >> 5;
+    // 1-D grid, KV head fastest: consecutive workgroups go to different XCDs, so all
+    // work items of one KV head share an XCD (and its L2) when Hk is a multiple of 8.
+    const int g = blockIdx.x % a.Hk, y = blockIdx.x / a.Hk;
+    const int T = a.T;
+
+    int head, pos, lb, le;
+    if constexpr (!SPARSE) {
+        const int qt = a.order[y];
+        const int R = w * 32 + l32;
+        head = g * a.G + R / a.BMq;
+        pos = qt * a.BMq + R % a.BMq;
+        lb = a.ptr[qt];
+        le = a.ptr[qt + 1];
+    } else {
+        const int hi = y / a.nb, qb = y - hi * a.nb;
+        head = g * a.G + hi;
+        pos = qb * a.sblock + w * 32 + l32;
+        const int r = head * a.nb + qb;
+        lb = a.ptr[r];
+        le = a.ptr[r + 1];
+    }
+    const bool row_ok = pos < T;
+    const int ntiles = (le - lb) * TPE;
+
+    // Q row fragments: B operand, lane holds dims 16*ks + 8*hf .. +7 of its row.
+    bf16x8 qf[8];
+    {
+        const bf16* qp = a.q + ((size_t)pos * a.Hq + head) * HEAD_DIM + 8 * hf;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            u32x4 x = {0u, 0u, 0u, 0u};
+            if (row_ok) x = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
+            qf[ks] = as_bf16x8(x);
+        }
+    }
+
+    f32x16 acc[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+    float m2 = -INFINITY, lsum = 0.f;
+
+    const bf16* kbase = a.k + (size_t)g * HEAD_DIM;
+    const bf16* vbase = a.v + (size_t)g * HEAD_DIM;
+    const size_t kv_row = (size_t)a.Hk * HEAD_DIM;
+
+    u32x4 kreg[KCH], v0reg[VUN], v1reg[VUN];
+    int4 dreg = {0, 0, 0, 0};
+    int nkey0 = 0;
+    bool nmask = false;
+
+    // Issue the global loads of tile t into registers.
+#define FWD_LOAD_TILE(t)                                                                       \
+    {                                                                                          \
+        const int e_ = a.ent[lb + (t) / TPE];                                                  \
+        bool full_;                                                                            \
+        if constexpr (SPARSE) {                                                                \
+            nkey0 = e_ * a.sblock + ((t) % TPE) * FWD_BN;                                      \
+            full_ = true;                                                                      \
+        } else {                                                                               \
+            nkey0 = (e_ >> 1) * FWD_BN;                                                        \
+            full_ = (e_ & 1) != 0;                                                             \
+        }                                                                                      \
+        nmask = !full_ || nkey0 + FWD_BN > T;                                                  \
+        _Pragma("unroll") for (int i = 0; i < KCH; ++i) {                                      \
+            const int c_ = tid + i * NT, key_ = nkey0 + (c_ >> 4);                             \
+            u32x4 x_ = {0u, 0u, 0u, 0u};                                                       \
+            if (key_ < T) x_ = *reinterpret_cast<const u32x4*>(kbase + key_ * kv_row + (c_ & 15) * 8); \
+            kreg[i] = x_;                                                                      \
+        }                                                                                      \
+        _Pragma("unroll") for (int i = 0; i < VUN; ++i) {                                      \
+            const int u_ = tid + i * NT, key_ = nkey0 + 2 * (u_ & 31), d0_ = (u_ >> 5) * 8;    \
+            u32x4 x0_ = {0u, 0u, 0u, 0u}, x1_ = {0u, 0u, 0u, 0u};                              \
+            if (key_ < T) x0_ = *reinterpret_cast<const u32x4*>(vbase + key_ * kv_row + d0_);  \
+            if (key_ + 1 < T) x1_ = *reinterpret_cast<const u32x4*>(vbase + (key_ + 1) * kv_row + d0_); \
+            v0reg[i] = x0_;                                                                    \
+            v1reg[i] = x1_;                                                                    \
+        }                                                                                      \
+        if (!SPARSE && nmask && tid < FWD_BN) {                                                \
+            const int key_ = nkey0 + tid;                                                      \
+            dreg = key_ < T ? a.desc[key_] : int4{0, 0, 0, 0};                                 \
+        }                                                                                      \
+    }
+
+    if (ntiles > 0) FWD_LOAD_TILE(0);
+
+    for (int t = 0; t < ntiles; ++t) {
+        const int key0 = nkey0;
+        const bool need_mask = nmask;
+
+        __syncthreads();   // every wave is done reading the previous tile
+#pragma unroll
+        for (int i = 0; i < KCH; ++i) {
+            const int c = tid + i * NT;
+            *reinterpret_cast<u32x4*>(&Ks[(c >> 4) * KS_LD + (c & 15) * 8]) = kreg[i];
+        }
+#pragma unroll
+        for (int i = 0; i < VUN; ++i) {
+            const int u = tid + i * NT, p = u & 31, d0 = (u >> 5) * 8;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const uint32_t x0 = v0reg[i][m], x1 = v1reg[i][m];
+                // (V[2p][d], V[2p+1][d]) for d = d0 + 2m and d0 + 2m + 1
+                *reinterpret_cast<uint32_t*>(&Vt[(d0 + 2 * m) * VT_LD + 2 * p]) = (x0 & 0xffffu) | (x1 << 16);
+                *reinterpret_cast<uint32_t*>(&Vt[(d0 + 2 * m + 1) * VT_LD + 2 * p]) = (x0 >> 16) | (x1 & 0xffff0000u);
+            }
+        }
+        if (!SPARSE && need_mask && tid < FWD_BN) Ds[tid] = dreg;
+        __syncthreads();
+
+        if (t + 1 < ntiles) FWD_LOAD_TILE(t + 1);
+
+        // S^T = K Q^T for the two 32-key halves of the tile.
+        f32x16 s[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+            const bf16* kr = Ks + (kb * 32 + l32) * KS_LD + 8 * hf;
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks)
+                s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(kr + 16 * ks), qf[ks], s[kb]);
+        }
+
+        if (need_mask) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int kk = kb * 32 + acc_row(r, hf);
+                    bool vis;
+                    if constexpr (SPARSE) {
+                        vis = key0 + kk < T;
+                    } else {
+                        const int4 d = Ds[kk];
+                        vis = (pos >= d.x && pos < d.y) || (pos >= d.z && pos < d.w);
+                    }
+                    if (!vis) s[kb][r] = -INFINITY;
+                }
+        }
+
+        // online softmax (base 2)
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+        mx = fmaxf(mx, swap_halves(mx));
+        const float cand = mx * a.c;
+        if (__ballot(cand > m2 + RESCALE_SLACK) != 0ull) {
+            const float mnew = fmaxf(m2, cand);
+            const float alpha = (m2 == -INFINITY) ? 0.f : fast_exp2(m2 - mnew);
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+            lsum *= alpha;
+            m2 = mnew;
+        }
+        const float msub = (m2 == -INFINITY) ? 0.f : m2;
+
+        bf16x8 pb[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            u32x4 pk;
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                const float p0 = fast_exp2(fmaf(s[kk >> 1][(kk & 1) * 8 + e], a.c, -msub));
+                const float p1 = fast_exp2(fmaf(s[kk >> 1][(kk & 1) * 8 + e + 1], a.c, -msub));
+                lsum += p0 + p1;
+                pk[e >> 1] = pack_bf16(p0, p1);
+            }
+            pb[kk] = as_bf16x8(pk);
+        }
+
+        // O^T += V^T P^T: key slot (hf, e) of step kk is key 16*kk + 8*(e/4) + 4*hf + e%4.
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+            const bf16* vr = Vt + (db * 32 + l32) * VT_LD + 4 * hf;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const u32x2 lo = *reinterpret_cast<const u32x2*>(vr + 16 * kk);
+                const u32x2 hi = *reinterpret_cast<const u32x2*>(vr + 16 * kk + 8);
+                const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
+                acc[db] = mfma32(as_bf16x8(av), pb[kk], acc[db]);
+            }
+        }
+    }
+#undef FWD_LOAD_TILE
+
+    const float ltot = lsum + swap_halves(lsum);
+    if (row_ok) {
+        const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+        bf16* op = a.o + ((size_t)pos * a.Hq + head) * HEAD_DIM;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const int d0 = db * 32 + 8 * i4 + 4 * hf;
+                u32x2 pk;
+                pk[0] = pack_bf16(acc[db][4 * i4 + 0] * inv, acc[db][4 * i4 + 1] * inv);
+                pk[1] = pack_bf16(acc[db][4 * i4 + 2] * inv, acc[db][4 * i4 + 3] * inv);
+                *reinterpret_cast<u32x2*>(op + d0) = pk;
+            }
+        if (hf == 0)
+            a.lse[(size_t)head * T + pos] = ltot > 0.f ? (m2 + fast_log2(ltot)) * LN2 : -INFINITY;
+    }
+}
+
+hipError_t launch_fwd(const Problem& P, const void* q, const void* k, const void* v, void* o, float* lse,
+                      const int4* desc, const void* index, hipStream_t s) {
+    const IndexLayout L = index_layout(P);
+    const char* base = static_cast<const char*>(index);
+    FwdArgs a;
+    a.q = static_cast<const bf16*>(q);
+    a.k = static_cast<const bf16*>(k);
+    a.v = static_cast<const bf16*>(v);
+    a.o = static_cast<bf16*>(o);
+    a.lse = lse;
+    a.desc = desc;
+    a.ptr = reinterpret_cast<const int*>(base + L.fwd_ptr);
+    a.ent = reinterpret_cast<const int*>(base + L.fwd_ent);
+    a.order = P.sparse ? nullptr : reinterpret_cast<const int*>(base + L.fwd_order);
+    a.T = P.T;
+    a.Hq = P.Hq;
+    a.Hk = P.Hk;
+    a.G = P.G;
+    a.BMq = P.fBM;
+    a.nb = P.nb;
+    a.sblock = P.sblock;
+    a.c = P.scale * LOG2E;
+    if (!P.sparse) {
+        hipLaunchKernelGGL((fwd_kernel<8, false>), dim3(P.Hk * P.nqt_f), dim3(512), 0, s, a);
+    } else if (P.sblock == 64) {
+        hipLaunchKernelGGL((fwd_kernel<2, true>), dim3(P.Hk * P.G * P.nb), dim3(128), 0, s, a);
+    } else {
+        hipLaunchKernelGGL((fwd_kernel<4, true>), dim3(P.Hk * P.G * P.nb), dim3(256), 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace mlct
