@@ -146,6 +146,7 @@ def main():
     desc_dev = torch.empty((T, 4), dtype=torch.int32, device=dev)
     keep_dev = torch.from_numpy(keep).to(dev) if sparse else None
     o = torch.empty((T, Hq, d), dtype=torch.bfloat16, device=dev)
+    o_lo = torch.empty((T, Hq, d), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((Hq, T), dtype=torch.float32, device=dev)
     dq = torch.empty((T, Hq, d), dtype=torch.float32, device=dev)
     dk = torch.empty((T, Hk, d), dtype=torch.float32, device=dev)
@@ -174,10 +175,11 @@ def main():
             ev[0].record(stream)
             attn.tile_index_build(prob, desc_dev.data_ptr(), index.data_ptr(), idx_bytes, sp)   # a2
         ev[1].record(stream)
-        attn.fwd(prob, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+        attn.fwd(prob, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), o_lo.data_ptr(), lse.data_ptr(),
                  0 if sparse else desc_dev.data_ptr(), index.data_ptr(), idx_bytes, 0, 0, sp)       # a3
         ev[2].record(stream)
-        attn.bwd_preprocess(prob, o.data_ptr(), do.data_ptr(), dq.data_ptr(), ws.data_ptr(), ws_bytes, sp)  # a4
+        attn.bwd_preprocess(prob, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), o_lo.data_ptr(),
+                            do.data_ptr(), dq.data_ptr(), ws.data_ptr(), ws_bytes, sp)                      # a4
         ev[3].record(stream)
         attn.bwd_main(prob, q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(), do.data_ptr(),
                       dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), 0 if sparse else desc_dev.data_ptr(),

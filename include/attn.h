@@ -186,36 +186,47 @@ attn_status attn_bwd_workspace_size(const attn_problem* prob, size_t* bytes_out)
 /*
  * Forward: O = softmax(scale * Q K^T + mask) V and LSE.
  *   q, k, v   : device bf16 inputs (layouts above)
- *   o         : device bf16 output [T][Hq][128]
+ *   o         : device bf16 output [T][Hq][128] (the fp32 result rounded to nearest even)
+ *   o_lo      : optional device bf16 output [T][Hq][128] (NULL: not written): the rounding
+ *               residual O_fp32 - o, so that o + o_lo carries the forward's fp32 O. Passed
+ *               to the backward it makes D = rowsum(dO * O) fp32-accurate.
  *   lse       : device fp32 output [Hq][T]
  *   desc_dev  : device descriptor (NULL for BLOCK_SPARSE)
  *   index_dev : tile / block index built for this problem
  *   ws        : workspace of attn_fwd_workspace_size bytes (may be NULL if that is 0)
  */
 attn_status attn_fwd(const attn_problem* prob, const void* q, const void* k, const void* v,
-                     void* o, float* lse, const int32_t* desc_dev,
+                     void* o, void* o_lo, float* lse, const int32_t* desc_dev,
                      const void* index_dev, size_t index_bytes,
                      void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Backward: gradients of L with dL/dO = dout, given the forward's O and LSE.
  * Equivalent to attn_bwd_preprocess followed by attn_bwd_main.
+ *   o, o_lo   : the forward's outputs (o_lo may be NULL: D then uses the bf16 O alone)
  *   dq        : device fp32 [T][Hq][128], overwritten
  *   dk, dv    : device fp32 [T][Hk][128], overwritten
- *   ws        : workspace of attn_bwd_workspace_size bytes (holds D = rowsum(dO * O))
+ *   ws        : workspace of attn_bwd_workspace_size bytes (D = rowsum(dO * O) and the
+ *               operand bounds of the preprocess)
+ * The three gradient products run on fp16 operands scaled by powers of two derived from
+ * max |Q|, max |K|, max ||dO_i|| and max ||V_j|| (measured by the preprocess), which keeps
+ * every operand in fp16 range; the scales are removed from the fp32 results.
  */
 attn_status attn_bwd(const attn_problem* prob, const void* q, const void* k, const void* v,
-                     const void* o, const float* lse, const void* dout,
+                     const void* o, const void* o_lo, const float* lse, const void* dout,
                      float* dq, float* dk, float* dv, const int32_t* desc_dev,
                      const void* index_dev, size_t index_bytes,
                      void* ws, size_t ws_bytes, void* stream);
 
 /*
- * Backward, first step: D[h][i] = sum_c dO[i][h][c] * O[i][h][c] into the workspace
- * (fp32 [Hq][T]) and dq cleared to zero (attn_bwd_main accumulates into it).
+ * Backward, first step: D[h][i] = sum_c dO[i][h][c] * (o + o_lo)[i][h][c] into the
+ * workspace (fp32 [Hq][T]), the operand bounds (max |Q|, max |K|, max ||dO_i||^2,
+ * max ||V_j||^2) after it, and dq cleared to zero (attn_bwd_main accumulates into it).
  */
-attn_status attn_bwd_preprocess(const attn_problem* prob, const void* o, const void* dout,
-                                float* dq, void* ws, size_t ws_bytes, void* stream);
+attn_status attn_bwd_preprocess(const attn_problem* prob, const void* q, const void* k,
+                                const void* v, const void* o, const void* o_lo,
+                                const void* dout, float* dq, void* ws, size_t ws_bytes,
+                                void* stream);
 
 /*
  * Backward, second step: recompute P on the non-empty tiles and accumulate

@@ -84,9 +84,9 @@ _SIGS = {
     "attn_block_index_build": (ctypes.c_int, [_PROB, _P, _P, _SZ, _P]),
     "attn_fwd_workspace_size": (ctypes.c_int, [_PROB, ctypes.POINTER(_SZ)]),
     "attn_bwd_workspace_size": (ctypes.c_int, [_PROB, ctypes.POINTER(_SZ)]),
-    "attn_fwd": (ctypes.c_int, [_PROB, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _SZ, _P]),
-    "attn_bwd": (ctypes.c_int, [_PROB, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _SZ, _P]),
-    "attn_bwd_preprocess": (ctypes.c_int, [_PROB, _P, _P, _P, _P, _SZ, _P]),
+    "attn_fwd": (ctypes.c_int, [_PROB, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _SZ, _P]),
+    "attn_bwd": (ctypes.c_int, [_PROB, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _SZ, _P]),
+    "attn_bwd_preprocess": (ctypes.c_int, [_PROB, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "attn_bwd_main": (ctypes.c_int, [_PROB, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _SZ, _P]),
     "attn_cast_bf16": (ctypes.c_int, [_P, _P, _SZ, _P]),
 }
@@ -198,18 +198,18 @@ def bwd_workspace_size(prob) -> int:
     return n.value
 
 
-def fwd(prob, q, k, v, o, lse, desc, index, index_bytes, ws, ws_bytes, stream=0):
-    _check(lib().attn_fwd(ctypes.byref(prob), q, k, v, o, lse, desc, index, index_bytes, ws, ws_bytes,
+def fwd(prob, q, k, v, o, o_lo, lse, desc, index, index_bytes, ws, ws_bytes, stream=0):
+    _check(lib().attn_fwd(ctypes.byref(prob), q, k, v, o, o_lo, lse, desc, index, index_bytes, ws, ws_bytes,
                           stream), "attn_fwd")
 
 
-def bwd(prob, q, k, v, o, lse, dout, dq, dk, dv, desc, index, index_bytes, ws, ws_bytes, stream=0):
-    _check(lib().attn_bwd(ctypes.byref(prob), q, k, v, o, lse, dout, dq, dk, dv, desc, index, index_bytes,
-                          ws, ws_bytes, stream), "attn_bwd")
+def bwd(prob, q, k, v, o, o_lo, lse, dout, dq, dk, dv, desc, index, index_bytes, ws, ws_bytes, stream=0):
+    _check(lib().attn_bwd(ctypes.byref(prob), q, k, v, o, o_lo, lse, dout, dq, dk, dv, desc, index,
+                          index_bytes, ws, ws_bytes, stream), "attn_bwd")
 
 
-def bwd_preprocess(prob, o, dout, dq, ws, ws_bytes, stream=0):
-    _check(lib().attn_bwd_preprocess(ctypes.byref(prob), o, dout, dq, ws, ws_bytes, stream),
+def bwd_preprocess(prob, q, k, v, o, o_lo, dout, dq, ws, ws_bytes, stream=0):
+    _check(lib().attn_bwd_preprocess(ctypes.byref(prob), q, k, v, o, o_lo, dout, dq, ws, ws_bytes, stream),
            "attn_bwd_preprocess")
 
 
@@ -237,6 +237,8 @@ class MaskedAttention:
         self.torch = torch
         self.T, self.Hq, self.Hk, self.spec = T, Hq, Hk, spec
         self.device = torch.device(device)
+        if self.device.type == "cuda" and self.device.index is None:
+            self.device = torch.device("cuda", torch.cuda.current_device())
         sparse = spec.kind == "block_sparse"
         self.prob = problem(T, Hq, Hk, spec.kind, spec.sparse_block if sparse else 0, scale)
         self.index_bytes = tile_index_size(self.prob)
@@ -264,19 +266,25 @@ class MaskedAttention:
     def _desc_ptr(self) -> int:
         return 0 if self.desc is None else self.desc.data_ptr()
 
-    def forward(self, q, k, v, o=None, lse=None):
+    def forward(self, q, k, v, o=None, lse=None, o_lo=None, with_o_lo=True):
+        """Returns (o, lse, o_lo); o_lo (the fp32 residual of O, for an accurate backward)
+        is None when with_o_lo is False."""
         torch = self.torch
         for t in (q, k, v):
-            assert t.dtype == torch.bfloat16 and t.is_contiguous() and t.device == self.device
+            if t.dtype != torch.bfloat16 or not t.is_contiguous() or t.device != self.device:
+                raise ValueError("q, k, v must be contiguous bf16 tensors on the problem's device")
         if o is None:
             o = torch.empty((self.T, self.Hq, 128), dtype=torch.bfloat16, device=self.device)
         if lse is None:
             lse = torch.empty((self.Hq, self.T), dtype=torch.float32, device=self.device)
-        fwd(self.prob, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+        if o_lo is None and with_o_lo:
+            o_lo = torch.empty((self.T, self.Hq, 128), dtype=torch.bfloat16, device=self.device)
+        fwd(self.prob, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+            0 if o_lo is None else o_lo.data_ptr(), lse.data_ptr(),
             self._desc_ptr(), self.index.data_ptr(), self.index_bytes, 0, 0, self._stream())
-        return o, lse
+        return o, lse, o_lo
 
-    def backward(self, q, k, v, o, lse, do, dq=None, dk=None, dv=None):
+    def backward(self, q, k, v, o, lse, do, o_lo=None, dq=None, dk=None, dv=None):
         torch = self.torch
         if dq is None:
             dq = torch.empty((self.T, self.Hq, 128), dtype=torch.float32, device=self.device)
@@ -284,7 +292,8 @@ class MaskedAttention:
             dk = torch.empty((self.T, self.Hk, 128), dtype=torch.float32, device=self.device)
         if dv is None:
             dv = torch.empty((self.T, self.Hk, 128), dtype=torch.float32, device=self.device)
-        bwd(self.prob, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), do.data_ptr(),
+        bwd(self.prob, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+            0 if o_lo is None else o_lo.data_ptr(), lse.data_ptr(), do.data_ptr(),
             dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), self._desc_ptr(), self.index.data_ptr(),
             self.index_bytes, self.bwd_ws.data_ptr(), self.bwd_ws_bytes, self._stream())
         return dq, dk, dv

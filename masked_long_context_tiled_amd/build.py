@@ -23,6 +23,8 @@ FLAGS = [
     # keep the compiler from emitting packed fp32 math
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result",
+    # keep MFMA accumulators in VGPRs (the default spills them to AGPRs with copies around every MFMA)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

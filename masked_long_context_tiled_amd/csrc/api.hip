@@ -35,6 +35,8 @@ attn_status validate_problem(const attn_problem* p, Problem* out) {
         if ((size_t)P.Hq * P.nb * P.nb > (size_t)INT32_MAX) return ATTN_ERR_UNSUPPORTED;
     } else {
         P.fBM = ROWS_PER_WG / G;
+        P.lgBM = 0;
+        while ((1 << P.lgBM) < P.fBM) ++P.lgBM;
         P.fBN = FWD_BN;
         P.bBM = ROWS_PER_WG / G;
         P.bBN = BWD_BN;
@@ -307,12 +309,12 @@ attn_status attn_bwd_workspace_size(const attn_problem* prob, size_t* bytes_out)
     attn_status st = validate_problem(prob, &P);
     if (st != ATTN_OK) return st;
     if (!bytes_out) return ATTN_ERR_INVALID_ARG;
-    *bytes_out = align256((size_t)P.Hq * P.T * sizeof(float));   // D = rowsum(dO * O), [Hq][T]
+    *bytes_out = bwd_workspace_bytes(P.Hq, P.T);   // D = rowsum(dO * O) [Hq][T] + operand bounds
     return ATTN_OK;
 }
 
 attn_status attn_fwd(const attn_problem* prob, const void* q, const void* k, const void* v, void* o,
-                     float* lse, const int32_t* desc_dev, const void* index_dev, size_t index_bytes,
+                     void* o_lo, float* lse, const int32_t* desc_dev, const void* index_dev, size_t index_bytes,
                      void* ws, size_t ws_bytes, void* stream) {
     (void)ws;
     (void)ws_bytes;
@@ -322,7 +324,7 @@ attn_status attn_fwd(const attn_problem* prob, const void* q, const void* k, con
     if (!q || !k || !v || !o || !lse || !index_dev) return ATTN_ERR_INVALID_ARG;
     if (!P.sparse && !desc_dev) return ATTN_ERR_INVALID_ARG;
     if (index_bytes < index_layout(P).total) return ATTN_ERR_WORKSPACE;
-    return hip_status(launch_fwd(P, q, k, v, o, lse, reinterpret_cast<const int4*>(desc_dev), index_dev,
+    return hip_status(launch_fwd(P, q, k, v, o, o_lo, lse, reinterpret_cast<const int4*>(desc_dev), index_dev,
                                  (hipStream_t)stream));
 }
 
@@ -332,14 +334,15 @@ static attn_status check_bwd_ws(const attn_problem* prob, const void* ws, size_t
     return (!ws || ws_bytes < need) ? ATTN_ERR_WORKSPACE : ATTN_OK;
 }
 
-attn_status attn_bwd_preprocess(const attn_problem* prob, const void* o, const void* dout, float* dq, void* ws,
+attn_status attn_bwd_preprocess(const attn_problem* prob, const void* q, const void* k, const void* v,
+                                const void* o, const void* o_lo, const void* dout, float* dq, void* ws,
                                 size_t ws_bytes, void* stream) {
     Problem P;
     attn_status st = validate_problem(prob, &P);
     if (st != ATTN_OK) return st;
-    if (!o || !dout || !dq) return ATTN_ERR_INVALID_ARG;
+    if (!q || !k || !v || !o || !dout || !dq) return ATTN_ERR_INVALID_ARG;
     if ((st = check_bwd_ws(prob, ws, ws_bytes)) != ATTN_OK) return st;
-    return hip_status(launch_bwd_pre(P, o, dout, dq, (float*)ws, (hipStream_t)stream));
+    return hip_status(launch_bwd_pre(P, q, k, v, o, o_lo, dout, dq, (float*)ws, (hipStream_t)stream));
 }
 
 attn_status attn_bwd_main(const attn_problem* prob, const void* q, const void* k, const void* v,
@@ -358,7 +361,7 @@ attn_status attn_bwd_main(const attn_problem* prob, const void* q, const void* k
 }
 
 attn_status attn_bwd(const attn_problem* prob, const void* q, const void* k, const void* v, const void* o,
-                     const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                     const void* o_lo, const float* lse, const void* dout, float* dq, float* dk, float* dv,
                      const int32_t* desc_dev, const void* index_dev, size_t index_bytes, void* ws,
                      size_t ws_bytes, void* stream) {
     Problem P;
@@ -370,7 +373,7 @@ attn_status attn_bwd(const attn_problem* prob, const void* q, const void* k, con
     if (!P.sparse && !desc_dev) return ATTN_ERR_INVALID_ARG;
     if (index_bytes < index_layout(P).total) return ATTN_ERR_WORKSPACE;
     if ((st = check_bwd_ws(prob, ws, ws_bytes)) != ATTN_OK) return st;
-    st = attn_bwd_preprocess(prob, o, dout, dq, ws, ws_bytes, stream);
+    st = attn_bwd_preprocess(prob, q, k, v, o, o_lo, dout, dq, ws, ws_bytes, stream);
     if (st != ATTN_OK) return st;
     return attn_bwd_main(prob, q, k, v, lse, dout, dq, dk, dv, desc_dev, index_dev, index_bytes, ws, ws_bytes,
                          stream);

@@ -32,6 +32,7 @@ struct FwdArgs {
     const bf16* k;
     const bf16* v;
     bf16* o;
+    bf16* o_lo;   // optional: bf16 residual of the fp32 O (O_fp32 - O)
     float* lse;
     const int4* desc;
     const int* ptr;
@@ -249,23 +250,32 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
     if (row_ok) {
         const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
         bf16* op = a.o + ((size_t)pos * a.Hq + head) * HEAD_DIM;
+        bf16* olp = a.o_lo ? a.o_lo + ((size_t)pos * a.Hq + head) * HEAD_DIM : nullptr;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
                 const int d0 = db * 32 + 8 * i4 + 4 * hf;
+                const float v0 = acc[db][4 * i4 + 0] * inv, v1 = acc[db][4 * i4 + 1] * inv;
+                const float v2 = acc[db][4 * i4 + 2] * inv, v3 = acc[db][4 * i4 + 3] * inv;
                 u32x2 pk;
-                pk[0] = pack_bf16(acc[db][4 * i4 + 0] * inv, acc[db][4 * i4 + 1] * inv);
-                pk[1] = pack_bf16(acc[db][4 * i4 + 2] * inv, acc[db][4 * i4 + 3] * inv);
+                pk[0] = pack_bf16(v0, v1);
+                pk[1] = pack_bf16(v2, v3);
                 *reinterpret_cast<u32x2*>(op + d0) = pk;
+                if (olp) {
+                    u32x2 lo;
+                    lo[0] = pack_bf16(v0 - bf16_lo(pk[0]), v1 - bf16_hi(pk[0]));
+                    lo[1] = pack_bf16(v2 - bf16_lo(pk[1]), v3 - bf16_hi(pk[1]));
+                    *reinterpret_cast<u32x2*>(olp + d0) = lo;
+                }
             }
         if (hf == 0)
             a.lse[(size_t)head * T + pos] = ltot > 0.f ? (m2 + fast_log2(ltot)) * LN2 : -INFINITY;
     }
 }
 
-hipError_t launch_fwd(const Problem& P, const void* q, const void* k, const void* v, void* o, float* lse,
-                      const int4* desc, const void* index, hipStream_t s) {
+hipError_t launch_fwd(const Problem& P, const void* q, const void* k, const void* v, void* o, void* o_lo,
+                      float* lse, const int4* desc, const void* index, hipStream_t s) {
     const IndexLayout L = index_layout(P);
     const char* base = static_cast<const char*>(index);
     FwdArgs a;
@@ -273,6 +283,7 @@ hipError_t launch_fwd(const Problem& P, const void* q, const void* k, const void
     a.k = static_cast<const bf16*>(k);
     a.v = static_cast<const bf16*>(v);
     a.o = static_cast<bf16*>(o);
+    a.o_lo = static_cast<bf16*>(o_lo);
     a.lse = lse;
     a.desc = desc;
     a.ptr = reinterpret_cast<const int*>(base + L.fwd_ptr);

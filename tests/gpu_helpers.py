@@ -31,11 +31,11 @@ def run_gpu(T, Hq, Hk, spec, keep=None, seed=0, backward=True, inputs=None):
     x = inputs if inputs is not None else attention_inputs(seed, T, Hq, Hk)
     q, k, v = (to_dev_bf16(x[n], torch) for n in ("q", "k", "v"))
     ma = attn.MaskedAttention(T, Hq, Hk, spec, keep=keep)
-    o, lse = ma.forward(q, k, v)
+    o, lse, o_lo = ma.forward(q, k, v)
     out = {"ma": ma}
     if backward:
         do = to_dev_bf16(x["do"], torch)
-        dq, dk, dv = ma.backward(q, k, v, o, lse, do)
+        dq, dk, dv = ma.backward(q, k, v, o, lse, do, o_lo=o_lo)
         torch.cuda.synchronize()
         out.update(dq=dq.cpu().numpy(), dk=dk.cpu().numpy(), dv=dv.cpu().numpy())
     torch.cuda.synchronize()

@@ -58,16 +58,16 @@ def test_entry_points_reject_before_launch():
     need = attn.tile_index_size(p)
     fake = 0x1000   # never dereferenced: validation fails first
     # null input pointer
-    assert L.attn_fwd(ctypes.byref(p), None, fake, fake, fake, fake, fake, fake, need, None, 0, None) == attn.ATTN_ERR_INVALID_ARG
+    assert L.attn_fwd(ctypes.byref(p), None, fake, fake, fake, None, fake, fake, fake, need, None, 0, None) == attn.ATTN_ERR_INVALID_ARG
     # missing descriptor for an interval mask
-    assert L.attn_fwd(ctypes.byref(p), fake, fake, fake, fake, fake, None, fake, need, None, 0, None) == attn.ATTN_ERR_INVALID_ARG
+    assert L.attn_fwd(ctypes.byref(p), fake, fake, fake, fake, None, fake, None, fake, need, None, 0, None) == attn.ATTN_ERR_INVALID_ARG
     # index buffer too small
-    assert L.attn_fwd(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, need - 1, None, 0, None) == attn.ATTN_ERR_WORKSPACE
+    assert L.attn_fwd(ctypes.byref(p), fake, fake, fake, fake, None, fake, fake, fake, need - 1, None, 0, None) == attn.ATTN_ERR_WORKSPACE
     assert L.attn_tile_index_build(ctypes.byref(p), fake, fake, need - 1, None) == attn.ATTN_ERR_WORKSPACE
     # backward workspace missing / too small
     ws = attn.bwd_workspace_size(p)
-    assert ws == 8 * 1024 * 4
-    args = [fake] * 10
+    assert ws >= 8 * 1024 * 4 + 16
+    args = [fake] * 4 + [None] + [fake] * 6   # q k v o | o_lo | lse dout dq dk dv desc
     assert L.attn_bwd(ctypes.byref(p), *args, fake, need, None, 0, None) == attn.ATTN_ERR_WORKSPACE
     assert L.attn_bwd(ctypes.byref(p), *args, fake, need, fake, ws - 1, None) == attn.ATTN_ERR_WORKSPACE
     # block index on a dense problem, tile index on a sparse problem
@@ -75,6 +75,9 @@ def test_entry_points_reject_before_launch():
     sp = attn.problem(1024, 8, 2, "block_sparse", 64)
     assert L.attn_tile_index_build(ctypes.byref(sp), fake, fake, attn.tile_index_size(sp), None) == attn.ATTN_ERR_INVALID_ARG
     assert L.attn_query_tile_shape(ctypes.byref(sp), *([ctypes.byref(ctypes.c_int32())] * 4)) == attn.ATTN_ERR_INVALID_ARG
+    assert L.attn_bwd_preprocess(ctypes.byref(p), fake, fake, fake, fake, None, fake, fake, fake, ws - 1, None) == attn.ATTN_ERR_WORKSPACE
+    assert L.attn_bwd_preprocess(ctypes.byref(p), None, fake, fake, fake, None, fake, fake, fake, ws, None) == attn.ATTN_ERR_INVALID_ARG
+    assert L.attn_bwd_main(ctypes.byref(p), *([fake] * 9), fake, need, fake, ws - 1, None) == attn.ATTN_ERR_WORKSPACE
     assert L.attn_cast_bf16(None, fake, 10, None) == attn.ATTN_ERR_INVALID_ARG
     assert L.attn_cast_bf16(None, None, 0, None) == attn.ATTN_OK
 
