@@ -27,8 +27,6 @@
 
 namespace mlct {
 
-constexpr int QS_LD = HEAD_DIM + 8;   // bf16 per Q / dO row in LDS
-constexpr int QT_LD = 32 + 8;         // fp16 per Q^T / dO^T row (32 query rows + pad)
 enum { ST_DO_NORM2 = 0, ST_V_NORM2 = 1, ST_Q_ABS = 2, ST_K_ABS = 3 };
 
 struct BwdArgs {
@@ -188,25 +186,75 @@ __device__ __forceinline__ RowMap row_map(const BwdArgs& a, int g, int e) {
     return m;
 }
 
-template <int NW, bool SPARSE>
-__global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a) {
-    constexpr int NT = NW * 64;
-    constexpr int KEYS = NW * 32;
-    constexpr int KT_LD = KEYS + 8;
-    constexpr int DS_LD = KEYS + 8;
-    constexpr int UPT = 256 / NT;   // (row pair, 8 dims) staging units per thread per row block
+// Transposed LDS read (ds_read_b64_tr_b16): within each group of 16 lanes, source lane s
+// supplies the address of 4 consecutive 16-bit elements and output lane i receives
+// element i % 4 of source lanes i/4, i/4 + 4, i/4 + 8, i/4 + 12. With source lane s
+// pointing at M[r0 + s/4][c0 + 4*(s%4)], output lane i gets M[r0 .. r0+3][c0 + i].
+__device__ __forceinline__ u32x2 ds_read_tr16(const _Float16* p) {
+    typedef short i16x4 __attribute__((ext_vector_type(4)));
+    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+    return __builtin_bit_cast(u32x2, v);
+}
 
-    __shared__ __attribute__((aligned(16))) bf16 Qs[32 * QS_LD];
-    __shared__ __attribute__((aligned(16))) bf16 dOs[32 * QS_LD];
-    __shared__ __attribute__((aligned(16))) _Float16 Kt[HEAD_DIM * KT_LD];
-    __shared__ __attribute__((aligned(16))) _Float16 Qt[HEAD_DIM * QT_LD];
-    __shared__ __attribute__((aligned(16))) _Float16 dOt[HEAD_DIM * QT_LD];
-    __shared__ __attribute__((aligned(16))) _Float16 dSs[32 * DS_LD];
-    __shared__ float lse_s[32];
-    __shared__ float dd_s[32];
+// Staged Q / dO rows: 128 fp16 (256 bytes) per row, the 16-byte chunk c of row q stored at
+// chunk slot c ^ 4*(q % 4) ^ (q / 4 % 4). Sixteen consecutive rows of one chunk (row
+// reads) and a 4-row x 4-chunk block (transposed reads) both land on distinct banks.
+__device__ __forceinline__ int swz(int q, int c) { return c ^ (4 * (q & 3)) ^ ((q >> 2) & 3); }
+__device__ __forceinline__ int swz_off(int q, int col) { return q * HEAD_DIM + swz(q, col >> 3) * 8 + (col & 7); }
+
+// A operand (32 rows x 16 k) whose row m = lane % 32 is column c0 + m of a swizzled
+// [rows][128] fp16 matrix M, k-slots e = 0..3 of the lane being rows r_lo + e and e = 4..7
+// rows r_hi + e - 4.
+__device__ __forceinline__ f16x8 tr_operand_swz(const _Float16* M, int r_lo, int r_hi, int c0, int lane) {
+    const int s = lane & 15;
+    const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (s & 3);
+    const u32x2 lo = ds_read_tr16(M + swz_off(r_lo + (s >> 2), col));
+    const u32x2 hi = ds_read_tr16(M + swz_off(r_hi + (s >> 2), col));
+    return as_f16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
+
+// Same for a plain [rows][ld] fp16 matrix.
+__device__ __forceinline__ f16x8 tr_operand(const _Float16* M, int ld, int r_lo, int r_hi, int c0, int lane) {
+    const int s = lane & 15;
+    const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (s & 3);
+    const u32x2 lo = ds_read_tr16(M + (r_lo + (s >> 2)) * ld + col);
+    const u32x2 hi = ds_read_tr16(M + (r_hi + (s >> 2)) * ld + col);
+    return as_f16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
+
+// 8 bf16 (one 16-byte chunk) -> 8 fp16 scaled by s.
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8_scaled(u32x4 x, float s) {
+    u32x4 r;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) r[m] = pack_f16(bf16_lo(x[m]) * s, bf16_hi(x[m]) * s);
+    return r;
+}
+
+// Work item: NWK blocks of 32 keys of one KV head, 2 * NWK waves. Waves 0..NWK-1 ("A")
+// compute S -> P and own dV^T and the dQ products; waves NWK..2*NWK-1 ("B") compute dP,
+// receive P through LDS, form dS and own dK^T. Wave w and w + NWK handle the same 32
+// keys and share a SIMD. All products run on fp16 operands: Q, K, V, dO are multiplied
+// by the powers of two sQ, sK, sV, sO while being staged.
+template <int NWK, bool SPARSE>
+__global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
+    constexpr int NT = NWK * 128;
+    constexpr int KEYS = NWK * 32;
+    constexpr int CPT = 512 / (NT / 2);     // 16-byte chunks per B thread per tensor per row block
+    constexpr int DST_LD = 32;              // fp16 per dS^T row (one key, 32 query rows)
+    constexpr int NDB = 4 / NWK;            // dQ dim blocks per A wave
+    constexpr int NKS = KEYS / 16;          // dQ k-steps
+
+    __shared__ __attribute__((aligned(16))) _Float16 Qh[32 * HEAD_DIM];    // swizzled rows
+    __shared__ __attribute__((aligned(16))) _Float16 dOh[32 * HEAD_DIM];   // swizzled rows
+    __shared__ __attribute__((aligned(16))) _Float16 Ps[NWK * 2 * 64 * 8];  // [kb][kk][lane][8]
+    __shared__ __attribute__((aligned(16))) _Float16 dSt[KEYS * DST_LD];
+    __shared__ __attribute__((aligned(16))) float lse_s[32];
+    __shared__ __attribute__((aligned(16))) float dd_s[32];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int l32 = lane & 31, hf = lane >> 5;
+    const bool is_a = w < NWK;
+    const int kb = is_a ? w : w - NWK;
     const int g = blockIdx.x % a.Hk, y = blockIdx.x / a.Hk;
     const int T = a.T;
 
@@ -215,6 +263,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a) {
     const float sO = pow2_scale(fmaxf(2.f * nrm_do * nrm_v, nrm_do));
     const float sQ = pow2_scale(a.stats[ST_Q_ABS]);
     const float sK = pow2_scale(a.stats[ST_K_ABS]);
+    const float sV = pow2_scale(nrm_v);
+    const float cS = a.c / (sQ * sK);       // exponent scale for the scaled scores
+    const float inv_sV = 1.f / sV;
 
     int key_base, col;
     if constexpr (!SPARSE) {
@@ -226,269 +277,268 @@ __global__ __launch_bounds__(NW * 64) void bwd_kernel(BwdArgs a) {
         col = g * a.nb + y;
     }
     const int lb = a.ptr[col], le = a.ptr[col + 1];
-    const int my_key = key_base + w * 32 + l32;
+    const int my_key = key_base + kb * 32 + l32;
     const bool key_ok = my_key < T;
     const size_t kv_row = (size_t)a.Hk * HEAD_DIM;
+    const bf16* kg = a.k + (size_t)g * HEAD_DIM;
+    const bf16* vg = a.v + (size_t)g * HEAD_DIM;
 
-    // K and V rows of this lane's key as B operands (dims 16*ks + 8*hf .. +7).
-    bf16x8 kf[8], vf[8];
-    {
-        const bf16* kp = a.k + (size_t)my_key * kv_row + (size_t)g * HEAD_DIM + 8 * hf;
-        const bf16* vp = a.v + (size_t)my_key * kv_row + (size_t)g * HEAD_DIM + 8 * hf;
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            u32x4 x = {0u, 0u, 0u, 0u}, z = {0u, 0u, 0u, 0u};
-            if (key_ok) {
-                x = *reinterpret_cast<const u32x4*>(kp + 16 * ks);
-                z = *reinterpret_cast<const u32x4*>(vp + 16 * ks);
-            }
-            kf[ks] = as_bf16x8(x);
-            vf[ks] = as_bf16x8(z);
-        }
-    }
-    int4 kd = {0, 0, 0, 0};
-    if (!SPARSE && key_ok) kd = a.desc[my_key];
-
-    // K^T of the whole key tile into LDS as fp16 * sK (B operand of dQ = dS K).
-    {
-        const bf16* kb = a.k + (size_t)g * HEAD_DIM;
-#pragma unroll
-        for (int i = 0; i < (KEYS * 8) / NT; ++i) {
-            const int u = tid + i * NT, p = u % (KEYS / 2), d0 = (u / (KEYS / 2)) * 8;
-            const int key = key_base + 2 * p;
-            u32x4 x0 = {0u, 0u, 0u, 0u}, x1 = {0u, 0u, 0u, 0u};
-            if (key < T) x0 = *reinterpret_cast<const u32x4*>(kb + (size_t)key * kv_row + d0);
-            if (key + 1 < T) x1 = *reinterpret_cast<const u32x4*>(kb + (size_t)(key + 1) * kv_row + d0);
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                *reinterpret_cast<uint32_t*>(&Kt[(d0 + 2 * m) * KT_LD + 2 * p]) =
-                    pack_f16(bf16_lo(x0[m]) * sK, bf16_lo(x1[m]) * sK);
-                *reinterpret_cast<uint32_t*>(&Kt[(d0 + 2 * m + 1) * KT_LD + 2 * p]) =
-                    pack_f16(bf16_hi(x0[m]) * sK, bf16_hi(x1[m]) * sK);
-            }
-        }
-    }
-
-    f32x16 dk_acc[4], dv_acc[4];
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            dk_acc[db][r] = 0.f;
-            dv_acc[db][r] = 0.f;
-        }
-
+    // A: K rows (B operand of S) and K^T fragments (B operand of dQ); B: V rows (B operand
+    // of dP). All fp16, scaled.
     const int RB = SPARSE ? a.sblock / 32 : ROWS_PER_WG / 32;   // 32-row blocks per list entry
     const int nsteps = (le - lb) * RB;
 
-    // prefetch registers: Q and dO rows (2 rows x 8 dims per unit), LSE and D
-    u32x4 px0[UPT], px1[UPT], py0[UPT], py1[UPT];
-    float pl = INFINITY, pd = 0.f;
+    // Both roles run the same number of steps with three barriers each:
+    //   b1: Q, dO, LSE, D of the row block staged (by B)
+    //   b2: P in LDS (A), dP in registers (B)
+    //   b3: dS^T in LDS (B)
+    // A: [b1] S, P -> LDS [b2] dV [b3] dQ     B: stage [b1] prefetch, dP [b2] dS, dK [b3]
+    // so A's dQ of one row block overlaps B's staging of the next.
+    f32x16 acc[4];   // A: dV^T, B: dK^T (dims db*32 + acc_row(r, hf), key = lane column)
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+
+    if (is_a) {
+        // K rows (B operand of S) and K^T fragments of the dQ dim blocks (B operand of dQ)
+        f16x8 kf[8];
+        u32x4 ktf[NDB * NKS];
+        {
+            const bf16* rowp = kg + (size_t)my_key * kv_row + 8 * hf;
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                u32x4 x = {0u, 0u, 0u, 0u};
+                if (key_ok) x = *reinterpret_cast<const u32x4*>(rowp + 16 * ks);
+                kf[ks] = as_f16x8(bf16x8_to_f16x8_scaled(x, sK));
+            }
+            const uint16_t* kb16 = reinterpret_cast<const uint16_t*>(kg);
+#pragma unroll
+            for (int i = 0; i < NDB; ++i) {
+                const int d = (kb + i * NWK) * 32 + l32;
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    u32x4 pk;
+#pragma unroll
+                    for (int e = 0; e < 8; e += 2) {
+                        const int k0 = key_base + 16 * ks + 8 * hf + e;
+                        const float x0 = k0 < T ? __uint_as_float((uint32_t)kb16[(size_t)k0 * kv_row + d] << 16) : 0.f;
+                        const float x1 = k0 + 1 < T ? __uint_as_float((uint32_t)kb16[(size_t)(k0 + 1) * kv_row + d] << 16) : 0.f;
+                        pk[e >> 1] = pack_f16(x0 * sK, x1 * sK);
+                    }
+                    ktf[i * NKS + ks] = pk;
+                }
+            }
+        }
+        int4 kd = {0, 0, 0, 0};
+        if (!SPARSE && key_ok) kd = a.desc[my_key];
+        const float dq_unscale = a.scale / (sO * sK);
+
+        for (int step = 0; step < nsteps; ++step) {
+            const int e = a.ent[lb + step / RB];
+            const int rb = step % RB;
+            const bool full = SPARSE ? true : ((e & 1) != 0);
+            const RowMap rm = row_map<SPARSE>(a, g, e);
+            lds_barrier();   // b1
+
+            // S = Q K^T (scaled by sQ * sK); rows q = acc_row(r, hf)
+            f32x16 sacc;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks)
+                sacc = mfma32h(*reinterpret_cast<const f16x8*>(&Qh[swz_off(l32, 16 * ks + 8 * hf)]), kf[ks], sacc);
+            uint32_t vis = key_ok ? 0xffffu : 0u;
+            if (!full && key_ok) {
+                vis = 0u;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int p = rm.pos(rb * 32 + acc_row(r, hf));
+                    const bool v = (p >= kd.x && p < kd.y) || (p >= kd.z && p < kd.w);
+                    vis |= (uint32_t)v << r;
+                }
+            }
+            // P (fp16); P and dS slots (hf, e) of step kk are rows 16*kk + 8*(e/4) + 4*hf + e%4
+            f16x8 pb[2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const float4 l0 = *reinterpret_cast<const float4*>(&lse_s[16 * kk + 4 * hf]);
+                const float4 l1 = *reinterpret_cast<const float4*>(&lse_s[16 * kk + 8 + 4 * hf]);
+                const float lr[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+                u32x4 pk;
+#pragma unroll
+                for (int e2 = 0; e2 < 8; e2 += 2) {
+                    const int r0 = kk * 8 + e2, r1 = r0 + 1;
+                    const float p0 = fast_exp2(fmaf(sacc[r0], cS, -lr[e2]));
+                    const float p1 = fast_exp2(fmaf(sacc[r1], cS, -lr[e2 + 1]));
+                    pk[e2 >> 1] = pack_f16(((vis >> r0) & 1u) ? p0 : 0.f, ((vis >> r1) & 1u) ? p1 : 0.f);
+                }
+                pb[kk] = as_f16x8(pk);
+                *reinterpret_cast<u32x4*>(&Ps[((kb * 2 + kk) * 64 + lane) * 8]) = pk;
+            }
+            lds_barrier();   // b2
+
+            // dV^T += (dO * sO)^T P
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+                    acc[db] = mfma32h(tr_operand_swz(dOh, 16 * kk + 4 * hf, 16 * kk + 8 + 4 * hf, db * 32, lane),
+                                      pb[kk], acc[db]);
+            lds_barrier();   // b3
+
+            // dQ[q][d] += scale * sum_key dS[q][key] K[key][d]: A = dS rows via transposed
+            // reads of dS^T (key slots 16*ks + 8*hf + e), B = K^T fragments in registers.
+            const int R0 = rb * 32;
+            const int p0 = rm.pos(R0);
+#pragma unroll
+            for (int i = 0; i < NDB; ++i) {
+                const int db = kb + i * NWK;
+                f32x16 qacc;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) qacc[r] = 0.f;
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+                    qacc = mfma32h(tr_operand(dSt, DST_LD, 16 * ks + 8 * hf, 16 * ks + 8 * hf + 4, 0, lane),
+                                   as_f16x8(ktf[i * NKS + ks]), qacc);
+                if (SPARSE || a.BMq >= 32) {
+                    float* dqp = a.dq + ((size_t)p0 * a.Hq + rm.head(R0)) * HEAD_DIM + db * 32 + l32;
+                    const size_t rs = (size_t)a.Hq * HEAD_DIM;
+                    if (p0 + 32 <= T) {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            unsafeAtomicAdd(dqp + (size_t)acc_row(r, hf) * rs, qacc[r] * dq_unscale);
+                    } else {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            if (p0 + acc_row(r, hf) < T)
+                                unsafeAtomicAdd(dqp + (size_t)acc_row(r, hf) * rs, qacc[r] * dq_unscale);
+                    }
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int R = R0 + acc_row(r, hf);
+                        const int p = rm.pos(R);
+                        if (p < T)
+                            unsafeAtomicAdd(a.dq + ((size_t)p * a.Hq + rm.head(R)) * HEAD_DIM + db * 32 + l32,
+                                            qacc[r] * dq_unscale);
+                    }
+                }
+            }
+        }
+    } else {
+        // V rows (B operand of dP)
+        f16x8 vf[8];
+        {
+            const bf16* rowp = vg + (size_t)my_key * kv_row + 8 * hf;
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                u32x4 x = {0u, 0u, 0u, 0u};
+                if (key_ok) x = *reinterpret_cast<const u32x4*>(rowp + 16 * ks);
+                vf[ks] = as_f16x8(bf16x8_to_f16x8_scaled(x, sV));
+            }
+        }
+        const int btid = tid - NWK * 64;
+        u32x4 pq[CPT], pdo[CPT];
+        float pl = INFINITY, pd = 0.f;
 
 #define BWD_LOAD_STEP(st)                                                                      \
     {                                                                                          \
         const int e_ = a.ent[lb + (st) / RB], rb_ = (st) % RB;                                 \
         const RowMap m_ = row_map<SPARSE>(a, g, e_);                                           \
-        _Pragma("unroll") for (int i = 0; i < UPT; ++i) {                                      \
-            const int u_ = tid + i * NT, q0_ = 2 * (u_ & 15), d0_ = (u_ >> 4) * 8;             \
-            const int R0_ = rb_ * 32 + q0_;                                                    \
-            const int p0_ = m_.pos(R0_), h0_ = m_.head(R0_);                                   \
-            const int p1_ = m_.pos(R0_ + 1), h1_ = m_.head(R0_ + 1);                           \
-            const size_t o0_ = ((size_t)p0_ * a.Hq + h0_) * HEAD_DIM + d0_;                    \
-            const size_t o1_ = ((size_t)p1_ * a.Hq + h1_) * HEAD_DIM + d0_;                    \
+        _Pragma("unroll") for (int i = 0; i < CPT; ++i) {                                      \
+            const int c_ = btid + i * (NT / 2), R_ = rb_ * 32 + (c_ >> 4), d0_ = (c_ & 15) * 8; \
+            const int p_ = m_.pos(R_);                                                         \
+            const size_t o_ = ((size_t)p_ * a.Hq + m_.head(R_)) * HEAD_DIM + d0_;              \
             u32x4 z_ = {0u, 0u, 0u, 0u};                                                       \
-            px0[i] = z_; py0[i] = z_; px1[i] = z_; py1[i] = z_;                                \
-            if (p0_ < T) {                                                                     \
-                px0[i] = *reinterpret_cast<const u32x4*>(a.q + o0_);                           \
-                py0[i] = *reinterpret_cast<const u32x4*>(a.dout + o0_);                        \
-            }                                                                                  \
-            if (p1_ < T) {                                                                     \
-                px1[i] = *reinterpret_cast<const u32x4*>(a.q + o1_);                           \
-                py1[i] = *reinterpret_cast<const u32x4*>(a.dout + o1_);                        \
+            pq[i] = z_;                                                                        \
+            pdo[i] = z_;                                                                       \
+            if (p_ < T) {                                                                      \
+                pq[i] = *reinterpret_cast<const u32x4*>(a.q + o_);                             \
+                pdo[i] = *reinterpret_cast<const u32x4*>(a.dout + o_);                         \
             }                                                                                  \
         }                                                                                      \
-        if (tid < 32) {                                                                        \
-            const int p_ = m_.pos(rb_ * 32 + tid), h_ = m_.head(rb_ * 32 + tid);               \
+        if (btid < 32) {                                                                       \
+            const int p_ = m_.pos(rb_ * 32 + btid), h_ = m_.head(rb_ * 32 + btid);             \
             pl = INFINITY; /* rows past the end and fully masked rows: P = 0 */                \
             pd = 0.f;                                                                          \
             if (p_ < T) {                                                                      \
                 const float lse_ = a.lse[(size_t)h_ * T + p_];                                 \
                 pl = lse_ == -INFINITY ? INFINITY : lse_ * LOG2E;                              \
-                pd = a.dbuf[(size_t)h_ * T + p_];                                              \
+                pd = a.dbuf[(size_t)h_ * T + p_] * sO;                                         \
             }                                                                                  \
         }                                                                                      \
     }
 
-    if (nsteps > 0) BWD_LOAD_STEP(0);
-
-    for (int step = 0; step < nsteps; ++step) {
-        const int e = a.ent[lb + step / RB];
-        const int rb = step % RB;
-        const bool full = SPARSE ? true : ((e & 1) != 0);
-        const RowMap rm = row_map<SPARSE>(a, g, e);
-
-        lds_barrier();   // previous row block fully consumed
-        // Stage: natural bf16 [q][d]; transposed fp16 [d][q] scaled by sQ / sO.
+        if (nsteps > 0) BWD_LOAD_STEP(0);
+        for (int step = 0; step < nsteps; ++step) {
+            // stage Q * sQ and dO * sO as swizzled fp16 rows, LSE (base 2) and D * sO
 #pragma unroll
-        for (int i = 0; i < UPT; ++i) {
-            const int u = tid + i * NT, q0 = 2 * (u & 15), d0 = (u >> 4) * 8;
-            *reinterpret_cast<u32x4*>(&Qs[q0 * QS_LD + d0]) = px0[i];
-            *reinterpret_cast<u32x4*>(&Qs[(q0 + 1) * QS_LD + d0]) = px1[i];
-            *reinterpret_cast<u32x4*>(&dOs[q0 * QS_LD + d0]) = py0[i];
-            *reinterpret_cast<u32x4*>(&dOs[(q0 + 1) * QS_LD + d0]) = py1[i];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                *reinterpret_cast<uint32_t*>(&Qt[(d0 + 2 * m) * QT_LD + q0]) =
-                    pack_f16(bf16_lo(px0[i][m]) * sQ, bf16_lo(px1[i][m]) * sQ);
-                *reinterpret_cast<uint32_t*>(&Qt[(d0 + 2 * m + 1) * QT_LD + q0]) =
-                    pack_f16(bf16_hi(px0[i][m]) * sQ, bf16_hi(px1[i][m]) * sQ);
-                *reinterpret_cast<uint32_t*>(&dOt[(d0 + 2 * m) * QT_LD + q0]) =
-                    pack_f16(bf16_lo(py0[i][m]) * sO, bf16_lo(py1[i][m]) * sO);
-                *reinterpret_cast<uint32_t*>(&dOt[(d0 + 2 * m + 1) * QT_LD + q0]) =
-                    pack_f16(bf16_hi(py0[i][m]) * sO, bf16_hi(py1[i][m]) * sO);
+            for (int i = 0; i < CPT; ++i) {
+                const int c = btid + i * (NT / 2), q = c >> 4, d0 = (c & 15) * 8;
+                *reinterpret_cast<u32x4*>(&Qh[swz_off(q, d0)]) = bf16x8_to_f16x8_scaled(pq[i], sQ);
+                *reinterpret_cast<u32x4*>(&dOh[swz_off(q, d0)]) = bf16x8_to_f16x8_scaled(pdo[i], sO);
             }
-        }
-        if (tid < 32) {
-            lse_s[tid] = pl;
-            dd_s[tid] = pd;
-        }
-        lds_barrier();
-
-        if (step + 1 < nsteps) BWD_LOAD_STEP(step + 1);
-
-        // S = Q K^T and dP = dO V^T: lane column = its key, rows q = acc_row(r, hf).
-        f32x16 sacc, dpacc;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            sacc[r] = 0.f;
-            dpacc[r] = 0.f;
-        }
-        {
-            const bf16* qr = Qs + l32 * QS_LD + 8 * hf;
-            const bf16* dr = dOs + l32 * QS_LD + 8 * hf;
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-                sacc = mfma32(*reinterpret_cast<const bf16x8*>(qr + 16 * ks), kf[ks], sacc);
-                dpacc = mfma32(*reinterpret_cast<const bf16x8*>(dr + 16 * ks), vf[ks], dpacc);
+            if (btid < 32) {
+                lse_s[btid] = pl;
+                dd_s[btid] = pd;
             }
-        }
+            lds_barrier();   // b1
+            if (step + 1 < nsteps) BWD_LOAD_STEP(step + 1);
 
-        // visibility of the 16 (row, key) cells of this lane: all of them on FULL tiles,
-        // the interval test on PARTIAL ones (the branch is uniform over the workgroup)
-        uint32_t vis = key_ok ? 0xffffu : 0u;
-        if (!full && key_ok) {
-            vis = 0u;
+            // dP = dO V^T (scaled by sO * sV)
+            f32x16 dpacc;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int p = rm.pos(rb * 32 + acc_row(r, hf));
-                const bool v = (p >= kd.x && p < kd.y) || (p >= kd.z && p < kd.w);
-                vis |= (uint32_t)v << r;
-            }
-        }
+            for (int r = 0; r < 16; ++r) dpacc[r] = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks)
+                dpacc = mfma32h(*reinterpret_cast<const f16x8*>(&dOh[swz_off(l32, 16 * ks + 8 * hf)]), vf[ks], dpacc);
+            lds_barrier();   // b2
 
-        // P (fp16, in [0, 1]) and dS * sO (fp16)
-        float ds[16];
-        f16x8 pb[2], sb[2];
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            u32x4 pk, sk;
-#pragma unroll
-            for (int e2 = 0; e2 < 8; e2 += 2) {
-                float pv[2];
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int r = kk * 8 + e2 + j;
-                    const int q = acc_row(r, hf);
-                    const float p = fast_exp2(fmaf(sacc[r], a.c, -lse_s[q]));
-                    pv[j] = ((vis >> r) & 1u) ? p : 0.f;
-                    ds[r] = pv[j] * (dpacc[r] - dd_s[q]) * sO;
-                }
-                pk[e2 >> 1] = pack_f16(pv[0], pv[1]);
-                sk[e2 >> 1] = pack_f16(ds[kk * 8 + e2], ds[kk * 8 + e2 + 1]);
-            }
-            pb[kk] = as_f16x8(pk);
-            sb[kk] = as_f16x8(sk);
-        }
-
-        // dV^T += dO^T P and dK^T += Q^T dS: query slot (hf, e) of step kk is row
-        // 16*kk + 8*(e/4) + 4*hf + e%4.
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-            const _Float16* dtr = dOt + (db * 32 + l32) * QT_LD + 4 * hf;
-            const _Float16* qtr = Qt + (db * 32 + l32) * QT_LD + 4 * hf;
+            // dS * sO = P * (dP * sO - D * sO); dK^T += (Q * sQ)^T (dS * sO); dS^T to LDS
+            f16x8 sb[2];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                const u32x2 a0 = *reinterpret_cast<const u32x2*>(dtr + 16 * kk);
-                const u32x2 a1 = *reinterpret_cast<const u32x2*>(dtr + 16 * kk + 8);
-                dv_acc[db] = mfma32h(as_f16x8(u32x4{a0[0], a0[1], a1[0], a1[1]}), pb[kk], dv_acc[db]);
-                const u32x2 b0 = *reinterpret_cast<const u32x2*>(qtr + 16 * kk);
-                const u32x2 b1 = *reinterpret_cast<const u32x2*>(qtr + 16 * kk + 8);
-                dk_acc[db] = mfma32h(as_f16x8(u32x4{b0[0], b0[1], b1[0], b1[1]}), sb[kk], dk_acc[db]);
-            }
-        }
-
-        // dS * sO (fp16) to LDS as [q][key] for dQ.
+                const f16x8 ph = as_f16x8(*reinterpret_cast<const u32x4*>(&Ps[((kb * 2 + kk) * 64 + lane) * 8]));
+                const float4 d0v = *reinterpret_cast<const float4*>(&dd_s[16 * kk + 4 * hf]);
+                const float4 d1v = *reinterpret_cast<const float4*>(&dd_s[16 * kk + 8 + 4 * hf]);
+                const float dr[8] = {d0v.x, d0v.y, d0v.z, d0v.w, d1v.x, d1v.y, d1v.z, d1v.w};
+                u32x4 sk;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dSs[acc_row(r, hf) * DS_LD + w * 32 + l32] = (_Float16)ds[r];
-        lds_barrier();
-
-        // dQ[q][d] += scale * sum_key dS[q][key] K[key][d]; wave w takes dim blocks w, w + NW, ...
-        const float dq_unscale = a.scale / (sO * sK);
-        for (int db = w; db < 4; db += NW) {
-            f32x16 qacc;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) qacc[r] = 0.f;
-            const _Float16* sr = dSs + l32 * DS_LD + 8 * hf;
-            const _Float16* kr = Kt + (db * 32 + l32) * KT_LD + 8 * hf;
-#pragma unroll
-            for (int ks = 0; ks < KEYS / 16; ++ks)
-                qacc = mfma32h(*reinterpret_cast<const f16x8*>(sr + 16 * ks),
-                               *reinterpret_cast<const f16x8*>(kr + 16 * ks), qacc);
-            // rows of a block are consecutive positions of one head unless G > 8
-            const int R0 = rb * 32;
-            const int p0 = rm.pos(R0);
-            if (SPARSE || a.BMq >= 32) {
-                float* dqp = a.dq + ((size_t)p0 * a.Hq + rm.head(R0)) * HEAD_DIM + db * 32 + l32;
-                const size_t rs = (size_t)a.Hq * HEAD_DIM;
-                if (p0 + 32 <= T) {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        unsafeAtomicAdd(dqp + (size_t)acc_row(r, hf) * rs, qacc[r] * dq_unscale);
-                } else {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r)
-                        if (p0 + acc_row(r, hf) < T)
-                            unsafeAtomicAdd(dqp + (size_t)acc_row(r, hf) * rs, qacc[r] * dq_unscale);
+                for (int e2 = 0; e2 < 8; e2 += 2) {
+                    const int r0 = kk * 8 + e2, r1 = r0 + 1;
+                    const float x0 = (float)ph[e2] * fmaf(dpacc[r0], inv_sV, -dr[e2]);
+                    const float x1 = (float)ph[e2 + 1] * fmaf(dpacc[r1], inv_sV, -dr[e2 + 1]);
+                    sk[e2 >> 1] = pack_f16(x0, x1);
                 }
-            } else {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int R = R0 + acc_row(r, hf);
-                    const int p = rm.pos(R);
-                    if (p < T)
-                        unsafeAtomicAdd(a.dq + ((size_t)p * a.Hq + rm.head(R)) * HEAD_DIM + db * 32 + l32,
-                                        qacc[r] * dq_unscale);
-                }
+                sb[kk] = as_f16x8(sk);
+                // rows 16*kk + 4*hf + 0..3 and 16*kk + 8 + 4*hf + 0..3 of this key's column
+                _Float16* dst = dSt + (kb * 32 + l32) * DST_LD + 16 * kk + 4 * hf;
+                *reinterpret_cast<u32x2*>(dst) = u32x2{sk[0], sk[1]};
+                *reinterpret_cast<u32x2*>(dst + 8) = u32x2{sk[2], sk[3]};
             }
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+                    acc[db] = mfma32h(tr_operand_swz(Qh, 16 * kk + 4 * hf, 16 * kk + 8 + 4 * hf, db * 32, lane),
+                                      sb[kk], acc[db]);
+            lds_barrier();   // b3
         }
-    }
 #undef BWD_LOAD_STEP
+    }
 
     if (key_ok) {
-        const float dk_unscale = a.scale / (sQ * sO), dv_unscale = 1.f / sO;
-        float* dkp = a.dk + (size_t)my_key * kv_row + (size_t)g * HEAD_DIM;
-        float* dvp = a.dv + (size_t)my_key * kv_row + (size_t)g * HEAD_DIM;
+        const float unscale = is_a ? 1.f / sO : a.scale / (sQ * sO);
+        float* outp = (is_a ? a.dv : a.dk) + (size_t)my_key * kv_row + (size_t)g * HEAD_DIM;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
                 const int d0 = db * 32 + 8 * i4 + 4 * hf;
-                *reinterpret_cast<float4*>(dkp + d0) =
-                    float4{dk_acc[db][4 * i4] * dk_unscale, dk_acc[db][4 * i4 + 1] * dk_unscale,
-                           dk_acc[db][4 * i4 + 2] * dk_unscale, dk_acc[db][4 * i4 + 3] * dk_unscale};
-                *reinterpret_cast<float4*>(dvp + d0) =
-                    float4{dv_acc[db][4 * i4] * dv_unscale, dv_acc[db][4 * i4 + 1] * dv_unscale,
-                           dv_acc[db][4 * i4 + 2] * dv_unscale, dv_acc[db][4 * i4 + 3] * dv_unscale};
+                *reinterpret_cast<float4*>(outp + d0) =
+                    float4{acc[db][4 * i4] * unscale, acc[db][4 * i4 + 1] * unscale,
+                           acc[db][4 * i4 + 2] * unscale, acc[db][4 * i4 + 3] * unscale};
             }
     }
 }
@@ -543,11 +593,11 @@ hipError_t launch_bwd_main(const Problem& P, const void* q, const void* k, const
     a.c = P.scale * LOG2E;
     a.scale = P.scale;
     if (!P.sparse) {
-        hipLaunchKernelGGL((bwd_kernel<4, false>), dim3(P.Hk * P.nkt_b), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((bwd_kernel<4, false>), dim3(P.Hk * P.nkt_b), dim3(512), 0, s, a);
     } else if (P.sblock == 64) {
-        hipLaunchKernelGGL((bwd_kernel<2, true>), dim3(P.Hk * P.nb), dim3(128), 0, s, a);
+        hipLaunchKernelGGL((bwd_kernel<2, true>), dim3(P.Hk * P.nb), dim3(256), 0, s, a);
     } else {
-        hipLaunchKernelGGL((bwd_kernel<4, true>), dim3(P.Hk * P.nb), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((bwd_kernel<4, true>), dim3(P.Hk * P.nb), dim3(512), 0, s, a);
     }
     return hipGetLastError();
 }
