@@ -4,7 +4,7 @@
 One step = one pass of the whole path over one batch of synthetic inputs that are
 already resident in HBM:
   column-interval descriptor (host) -> device copy -> tile index (classifier + lists)
-  -> attn_fwd -> attn_bwd_preprocess (D = rowsum(dO*O), dQ cleared) -> attn_bwd_main.
+  -> attn_fwd -> attn_bwd_preprocess (D = rowsum(dO*O), operand bounds) -> attn_bwd_main.
 The default workload is CAUSAL at T = 8192, 64 query heads sharing 8 KV heads, head
 dim 128, bf16 inputs N(0,1) from a seed.
 
@@ -179,7 +179,7 @@ def main():
                  0 if sparse else desc_dev.data_ptr(), index.data_ptr(), idx_bytes, 0, 0, sp)       # a3
         ev[2].record(stream)
         attn.bwd_preprocess(prob, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), o_lo.data_ptr(),
-                            do.data_ptr(), dq.data_ptr(), ws.data_ptr(), ws_bytes, sp)                      # a4
+                            do.data_ptr(), ws.data_ptr(), ws_bytes, sp)                                     # a4
         ev[3].record(stream)
         attn.bwd_main(prob, q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(), do.data_ptr(),
                       dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), 0 if sparse else desc_dev.data_ptr(),

@@ -220,19 +220,19 @@ attn_status attn_bwd(const attn_problem* prob, const void* q, const void* k, con
 
 /*
  * Backward, first step: D[h][i] = sum_c dO[i][h][c] * (o + o_lo)[i][h][c] into the
- * workspace (fp32 [Hq][T]), the operand bounds (max |Q|, max |K|, max ||dO_i||^2,
- * max ||V_j||^2) after it, and dq cleared to zero (attn_bwd_main accumulates into it).
+ * workspace (fp32 [Hq][T]) and the operand bounds (max |Q|, max |K|, max ||dO_i||^2,
+ * max ||V_j||^2) after it.
  */
 attn_status attn_bwd_preprocess(const attn_problem* prob, const void* q, const void* k,
                                 const void* v, const void* o, const void* o_lo,
-                                const void* dout, float* dq, void* ws, size_t ws_bytes,
-                                void* stream);
+                                const void* dout, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * Backward, second step: recompute P on the non-empty tiles and accumulate
- * dV = P^T dO, dK = scale * dS^T Q (written once per key) and dQ += scale * dS K
- * (added into dq), with dS = P * (dO V^T - D). Requires attn_bwd_preprocess on the
- * same ws / dq first (stream order).
+ * Backward, second step: recompute P on the non-empty tiles and write dV = P^T dO and
+ * dK = scale * dS^T Q (key-tile major, each key written once) and dQ = scale * dS K
+ * (query-tile major, each row written once), with dS = P * (dO V^T - D). No atomics: the
+ * gradients are deterministic. Requires attn_bwd_preprocess on the same ws first (stream
+ * order).
  */
 attn_status attn_bwd_main(const attn_problem* prob, const void* q, const void* k, const void* v,
                           const float* lse, const void* dout,

@@ -86,7 +86,7 @@ _SIGS = {
     "attn_bwd_workspace_size": (ctypes.c_int, [_PROB, ctypes.POINTER(_SZ)]),
     "attn_fwd": (ctypes.c_int, [_PROB, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _SZ, _P]),
     "attn_bwd": (ctypes.c_int, [_PROB, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _SZ, _P]),
-    "attn_bwd_preprocess": (ctypes.c_int, [_PROB, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "attn_bwd_preprocess": (ctypes.c_int, [_PROB, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "attn_bwd_main": (ctypes.c_int, [_PROB, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _SZ, _P]),
     "attn_cast_bf16": (ctypes.c_int, [_P, _P, _SZ, _P]),
 }
@@ -208,8 +208,8 @@ def bwd(prob, q, k, v, o, o_lo, lse, dout, dq, dk, dv, desc, index, index_bytes,
                           index_bytes, ws, ws_bytes, stream), "attn_bwd")
 
 
-def bwd_preprocess(prob, q, k, v, o, o_lo, dout, dq, ws, ws_bytes, stream=0):
-    _check(lib().attn_bwd_preprocess(ctypes.byref(prob), q, k, v, o, o_lo, dout, dq, ws, ws_bytes, stream),
+def bwd_preprocess(prob, q, k, v, o, o_lo, dout, ws, ws_bytes, stream=0):
+    _check(lib().attn_bwd_preprocess(ctypes.byref(prob), q, k, v, o, o_lo, dout, ws, ws_bytes, stream),
            "attn_bwd_preprocess")
 
 

@@ -335,14 +335,14 @@ static attn_status check_bwd_ws(const attn_problem* prob, const void* ws, size_t
 }
 
 attn_status attn_bwd_preprocess(const attn_problem* prob, const void* q, const void* k, const void* v,
-                                const void* o, const void* o_lo, const void* dout, float* dq, void* ws,
-                                size_t ws_bytes, void* stream) {
+                                const void* o, const void* o_lo, const void* dout, void* ws, size_t ws_bytes,
+                                void* stream) {
     Problem P;
     attn_status st = validate_problem(prob, &P);
     if (st != ATTN_OK) return st;
-    if (!q || !k || !v || !o || !dout || !dq) return ATTN_ERR_INVALID_ARG;
+    if (!q || !k || !v || !o || !dout) return ATTN_ERR_INVALID_ARG;
     if ((st = check_bwd_ws(prob, ws, ws_bytes)) != ATTN_OK) return st;
-    return hip_status(launch_bwd_pre(P, q, k, v, o, o_lo, dout, dq, (float*)ws, (hipStream_t)stream));
+    return hip_status(launch_bwd_pre(P, q, k, v, o, o_lo, dout, (float*)ws, (hipStream_t)stream));
 }
 
 attn_status attn_bwd_main(const attn_problem* prob, const void* q, const void* k, const void* v,
@@ -373,7 +373,7 @@ attn_status attn_bwd(const attn_problem* prob, const void* q, const void* k, con
     if (!P.sparse && !desc_dev) return ATTN_ERR_INVALID_ARG;
     if (index_bytes < index_layout(P).total) return ATTN_ERR_WORKSPACE;
     if ((st = check_bwd_ws(prob, ws, ws_bytes)) != ATTN_OK) return st;
-    st = attn_bwd_preprocess(prob, q, k, v, o, o_lo, dout, dq, ws, ws_bytes, stream);
+    st = attn_bwd_preprocess(prob, q, k, v, o, o_lo, dout, ws, ws_bytes, stream);
     if (st != ATTN_OK) return st;
     return attn_bwd_main(prob, q, k, v, lse, dout, dq, dk, dv, desc_dev, index_dev, index_bytes, ws, ws_bytes,
                          stream);

@@ -3,26 +3,30 @@
 //   D_i  = sum_c dO[i, c] O[i, c]                              (bwd_pre_kernel, HBM-bound)
 //   P    = exp(scale * Q K^T - LSE)  on the non-empty tiles    (recomputed)
 //   dV  += P^T dO,  dP = dO V^T,  dS = P * (dP - D)
-//   dK  += scale * dS^T Q,  dQ += scale * dS K                 (bwd_kernel)
+//   dK  += scale * dS^T Q                                      (bwd_kernel, key-tile major)
+//   dQ   = scale * dS K                                        (dq_kernel, query-tile major)
 //
-// Work item = one workgroup = 32 * NW keys of one KV head. Each wave keeps its 32 keys'
-// K and V rows in registers (B operands of S and dP) and accumulates dK^T, dV^T for them
-// over every non-empty query tile of the key tile's list and every query head of the
-// group, so dK and dV are written once, without atomics. Query rows are processed 32 at a
-// time, the next block's Q and dO prefetched into registers while the current one
-// computes: they are staged in LDS in natural layout (A operands of S and dP) and
-// transposed (A operands of dK^T and dV^T). S is computed untransposed, so P and dS come
-// out of the accumulators already in the B-operand layout of the dK^T/dV^T products. dS
-// goes through LDS once more for dQ = dS K (K^T staged once per work item); each row
-// block's dQ partial is added to the fp32 output with hardware float atomics.
+// bwd_kernel. Work item = 32 * NWK keys of one KV head, walking the non-empty query tiles
+// of its key tile's list for every query head of the group, 32 query rows per step. It
+// runs 2 * NWK waves (two per SIMD) in two roles on the same 32 keys: "A" waves compute
+// S = Q K^T -> P and accumulate dV^T = dO^T P; "B" waves compute dP = dO V^T, receive P
+// through LDS, form dS = P * (dP - D) and accumulate dK^T = Q^T dS. Each role keeps its
+// keys' K or V rows in registers (B operands) and its 128 x 32 accumulator, so dK and dV
+// are written once, without atomics. The B waves prefetch and stage the row blocks; S and
+// dP are computed untransposed so P and dS leave the accumulators already in the B-operand
+// layout of the dV^T / dK^T products, whose A operands (dO^T, Q^T) come from transposed
+// LDS reads of the staged rows.
 //
-// Precision. S and dP use the bf16 inputs as they are. The three gradient products
-// (P^T dO, dS^T Q, dS K) take fp16 operands: fp16 carries 11 significant bits against
-// bf16's 8, which cuts the rounding of P and dS by 8x. To keep every fp16 operand inside
-// fp16's range, dO, Q and K are multiplied by powers of two chosen from bounds measured in
-// the preprocess (max |Q|, max |K|, max ||dO_i||, max ||V_j||; |dS_ij| <= 2 ||dO_i||
-// max_j ||V_j|| bounds dS), and the scales are divided out of the fp32 results.
-// D uses O plus its low half O_lo when the forward wrote one, i.e. the forward's fp32 O.
+// dq_kernel. dQ in its own pass, query-tile major on the forward's tile lists (described
+// at the kernel), so dQ needs no atomics and is deterministic.
+//
+// Precision. All products take fp16 operands: fp16 carries 11 significant bits against
+// bf16's 8, which cuts the rounding of P and dS by 8x, and bf16 inputs convert exactly
+// within range. To keep every operand inside fp16's range, Q, K, V and dO are multiplied
+// by powers of two chosen from bounds measured in the preprocess (max |Q|, max |K|,
+// max ||V_j||, max ||dO_i||; |dS_ij| <= 2 ||dO_i|| max_j ||V_j|| bounds dS), and the
+// scales are divided out of the fp32 results. D uses O plus its low half O_lo when the
+// forward wrote one, i.e. the forward's fp32 O.
 #include "common.h"
 
 namespace mlct {
@@ -78,12 +82,9 @@ __device__ __forceinline__ void block_max_to(float* p, float v) {
     if (threadIdx.x == 0) atomic_max_nonneg(p, fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3])));
 }
 
-// dq = 0 and the bound slots = 0.
-__global__ void zero_kernel(float4* __restrict__ p, size_t n4, float* __restrict__ stats) {
-    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const size_t stride = (size_t)gridDim.x * blockDim.x;
-    if (i < BWD_STATS) stats[i] = 0.f;
-    for (size_t j = i; j < n4; j += stride) p[j] = float4{0.f, 0.f, 0.f, 0.f};
+// The bound slots = 0 (a kernel rather than a memset, so the sequence can be captured).
+__global__ void zero_stats_kernel(float* __restrict__ stats) {
+    if (threadIdx.x < BWD_STATS) stats[threadIdx.x] = 0.f;
 }
 
 // D[h][i] = sum_c dO[i][h][c] * (O + O_lo)[i][h][c], and max_i ||dO_i||^2.
@@ -240,14 +241,10 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
     constexpr int NT = NWK * 128;
     constexpr int KEYS = NWK * 32;
     constexpr int CPT = 512 / (NT / 2);     // 16-byte chunks per B thread per tensor per row block
-    constexpr int DST_LD = 32;              // fp16 per dS^T row (one key, 32 query rows)
-    constexpr int NDB = 4 / NWK;            // dQ dim blocks per A wave
-    constexpr int NKS = KEYS / 16;          // dQ k-steps
 
     __shared__ __attribute__((aligned(16))) _Float16 Qh[32 * HEAD_DIM];    // swizzled rows
     __shared__ __attribute__((aligned(16))) _Float16 dOh[32 * HEAD_DIM];   // swizzled rows
     __shared__ __attribute__((aligned(16))) _Float16 Ps[NWK * 2 * 64 * 8];  // [kb][kk][lane][8]
-    __shared__ __attribute__((aligned(16))) _Float16 dSt[KEYS * DST_LD];
     __shared__ __attribute__((aligned(16))) float lse_s[32];
     __shared__ __attribute__((aligned(16))) float dd_s[32];
 
@@ -291,9 +288,8 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
     // Both roles run the same number of steps with three barriers each:
     //   b1: Q, dO, LSE, D of the row block staged (by B)
     //   b2: P in LDS (A), dP in registers (B)
-    //   b3: dS^T in LDS (B)
-    // A: [b1] S, P -> LDS [b2] dV [b3] dQ     B: stage [b1] prefetch, dP [b2] dS, dK [b3]
-    // so A's dQ of one row block overlaps B's staging of the next.
+    //   b3: every reader of the staged rows is done
+    // A: [b1] S, P -> LDS [b2] dV [b3]        B: stage [b1] prefetch, dP [b2] dS, dK [b3]
     f32x16 acc[4];   // A: dV^T, B: dK^T (dims db*32 + acc_row(r, hf), key = lane column)
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -301,9 +297,8 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
         for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
     if (is_a) {
-        // K rows (B operand of S) and K^T fragments of the dQ dim blocks (B operand of dQ)
+        // K rows (B operand of S)
         f16x8 kf[8];
-        u32x4 ktf[NDB * NKS];
         {
             const bf16* rowp = kg + (size_t)my_key * kv_row + 8 * hf;
 #pragma unroll
@@ -312,27 +307,9 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
                 if (key_ok) x = *reinterpret_cast<const u32x4*>(rowp + 16 * ks);
                 kf[ks] = as_f16x8(bf16x8_to_f16x8_scaled(x, sK));
             }
-            const uint16_t* kb16 = reinterpret_cast<const uint16_t*>(kg);
-#pragma unroll
-            for (int i = 0; i < NDB; ++i) {
-                const int d = (kb + i * NWK) * 32 + l32;
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
-                    u32x4 pk;
-#pragma unroll
-                    for (int e = 0; e < 8; e += 2) {
-                        const int k0 = key_base + 16 * ks + 8 * hf + e;
-                        const float x0 = k0 < T ? __uint_as_float((uint32_t)kb16[(size_t)k0 * kv_row + d] << 16) : 0.f;
-                        const float x1 = k0 + 1 < T ? __uint_as_float((uint32_t)kb16[(size_t)(k0 + 1) * kv_row + d] << 16) : 0.f;
-                        pk[e >> 1] = pack_f16(x0 * sK, x1 * sK);
-                    }
-                    ktf[i * NKS + ks] = pk;
-                }
-            }
         }
         int4 kd = {0, 0, 0, 0};
         if (!SPARSE && key_ok) kd = a.desc[my_key];
-        const float dq_unscale = a.scale / (sO * sK);
 
         for (int step = 0; step < nsteps; ++step) {
             const int e = a.ent[lb + step / RB];
@@ -386,45 +363,6 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
                     acc[db] = mfma32h(tr_operand_swz(dOh, 16 * kk + 4 * hf, 16 * kk + 8 + 4 * hf, db * 32, lane),
                                       pb[kk], acc[db]);
             lds_barrier();   // b3
-
-            // dQ[q][d] += scale * sum_key dS[q][key] K[key][d]: A = dS rows via transposed
-            // reads of dS^T (key slots 16*ks + 8*hf + e), B = K^T fragments in registers.
-            const int R0 = rb * 32;
-            const int p0 = rm.pos(R0);
-#pragma unroll
-            for (int i = 0; i < NDB; ++i) {
-                const int db = kb + i * NWK;
-                f32x16 qacc;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) qacc[r] = 0.f;
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks)
-                    qacc = mfma32h(tr_operand(dSt, DST_LD, 16 * ks + 8 * hf, 16 * ks + 8 * hf + 4, 0, lane),
-                                   as_f16x8(ktf[i * NKS + ks]), qacc);
-                if (SPARSE || a.BMq >= 32) {
-                    float* dqp = a.dq + ((size_t)p0 * a.Hq + rm.head(R0)) * HEAD_DIM + db * 32 + l32;
-                    const size_t rs = (size_t)a.Hq * HEAD_DIM;
-                    if (p0 + 32 <= T) {
-#pragma unroll
-                        for (int r = 0; r < 16; ++r)
-                            unsafeAtomicAdd(dqp + (size_t)acc_row(r, hf) * rs, qacc[r] * dq_unscale);
-                    } else {
-#pragma unroll
-                        for (int r = 0; r < 16; ++r)
-                            if (p0 + acc_row(r, hf) < T)
-                                unsafeAtomicAdd(dqp + (size_t)acc_row(r, hf) * rs, qacc[r] * dq_unscale);
-                    }
-                } else {
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int R = R0 + acc_row(r, hf);
-                        const int p = rm.pos(R);
-                        if (p < T)
-                            unsafeAtomicAdd(a.dq + ((size_t)p * a.Hq + rm.head(R)) * HEAD_DIM + db * 32 + l32,
-                                            qacc[r] * dq_unscale);
-                    }
-                }
-            }
         }
     } else {
         // V rows (B operand of dP)
@@ -495,7 +433,7 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
                 dpacc = mfma32h(*reinterpret_cast<const f16x8*>(&dOh[swz_off(l32, 16 * ks + 8 * hf)]), vf[ks], dpacc);
             lds_barrier();   // b2
 
-            // dS * sO = P * (dP * sO - D * sO); dK^T += (Q * sQ)^T (dS * sO); dS^T to LDS
+            // dS * sO = P * (dP * sO - D * sO); dK^T += (Q * sQ)^T (dS * sO)
             f16x8 sb[2];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
@@ -512,10 +450,6 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
                     sk[e2 >> 1] = pack_f16(x0, x1);
                 }
                 sb[kk] = as_f16x8(sk);
-                // rows 16*kk + 4*hf + 0..3 and 16*kk + 8 + 4*hf + 0..3 of this key's column
-                _Float16* dst = dSt + (kb * 32 + l32) * DST_LD + 16 * kk + 4 * hf;
-                *reinterpret_cast<u32x2*>(dst) = u32x2{sk[0], sk[1]};
-                *reinterpret_cast<u32x2*>(dst + 8) = u32x2{sk[2], sk[3]};
             }
 #pragma unroll
             for (int db = 0; db < 4; ++db)
@@ -543,11 +477,216 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
     }
 }
 
+// dQ pass: dQ = scale * dS K, one query tile per work item, no atomics.
+//
+// Work item and tile lists are the forward's: 32 * NW (head, position) rows (the G heads
+// of one KV head x 256/G positions, or one block-sparse (head, query block) row) walking
+// 64-key tiles. Like the forward it works on transposed products so a lane owns one query
+// row: S^T = K Q^T and dP^T = V dO^T (A = K / V rows from LDS, B = the wave's Q / dO rows
+// in registers), then P^T, dS^T = P^T * (dP^T - D) with the row's LSE and D as per-lane
+// scalars, and dQ^T += K^T dS^T with K^T read from the same LDS tile by transposed reads
+// and dS^T straight from the accumulators as the B operand. Operands are fp16 scaled by
+// the same powers of two as the main backward kernel.
+template <int NW, bool SPARSE>
+__global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
+    constexpr int NT = NW * 64;
+    constexpr int CPT = 1024 / NT;               // 16-byte chunks per thread per tile per tensor
+    constexpr int TPE = SPARSE ? NW / 2 : 1;     // 64-key tiles per list entry
+
+    __shared__ __attribute__((aligned(16))) _Float16 Kh[FWD_BN * HEAD_DIM];   // swizzled rows
+    __shared__ __attribute__((aligned(16))) _Float16 Vh[FWD_BN * HEAD_DIM];   // swizzled rows
+    __shared__ int4 Ds[FWD_BN];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int l32 = lane & 31, hf = lane >> 5;
+    const int g = blockIdx.x % a.Hk, y = blockIdx.x / a.Hk;
+    const int T = a.T;
+
+    const float nrm_do = sqrtf(a.stats[ST_DO_NORM2]), nrm_v = sqrtf(a.stats[ST_V_NORM2]);
+    const float sO = pow2_scale(fmaxf(2.f * nrm_do * nrm_v, nrm_do));
+    const float sQ = pow2_scale(a.stats[ST_Q_ABS]);
+    const float sK = pow2_scale(a.stats[ST_K_ABS]);
+    const float sV = pow2_scale(nrm_v);
+    const float cS = a.c / (sQ * sK);
+    const float inv_sV = 1.f / sV;
+
+    int head, pos, lb, le;
+    if constexpr (!SPARSE) {
+        const int qt = a.order[y];
+        const int R = w * 32 + l32;
+        head = g * a.G + (R >> a.lgBMq);
+        pos = qt * a.BMq + (R & (a.BMq - 1));
+        lb = a.ptr[qt];
+        le = a.ptr[qt + 1];
+    } else {
+        const int hi = y / a.nb, qb = y - hi * a.nb;
+        head = g * a.G + hi;
+        pos = qb * a.sblock + w * 32 + l32;
+        const int r = head * a.nb + qb;
+        lb = a.ptr[r];
+        le = a.ptr[r + 1];
+    }
+    const bool row_ok = pos < T;
+    const int ntiles = (le - lb) * TPE;
+
+    // this lane's row: LSE (base 2), D * sO, Q * sQ and dO * sO as B operands
+    float lse2 = INFINITY, dd = 0.f;
+    f16x8 qf[8], df[8];
+    {
+        const size_t ro = ((size_t)pos * a.Hq + head) * HEAD_DIM + 8 * hf;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            u32x4 x = {0u, 0u, 0u, 0u}, z = {0u, 0u, 0u, 0u};
+            if (row_ok) {
+                x = *reinterpret_cast<const u32x4*>(a.q + ro + 16 * ks);
+                z = *reinterpret_cast<const u32x4*>(a.dout + ro + 16 * ks);
+            }
+            qf[ks] = as_f16x8(bf16x8_to_f16x8_scaled(x, sQ));
+            df[ks] = as_f16x8(bf16x8_to_f16x8_scaled(z, sO));
+        }
+        if (row_ok) {
+            const float l = a.lse[(size_t)head * T + pos];
+            lse2 = l == -INFINITY ? INFINITY : l * LOG2E;
+            dd = a.dbuf[(size_t)head * T + pos] * sO;
+        }
+    }
+
+    f32x16 acc[4];   // dQ^T: dims db*32 + acc_row(r, hf), query = lane column
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+
+    const bf16* kbase = a.k + (size_t)g * HEAD_DIM;
+    const bf16* vbase = a.v + (size_t)g * HEAD_DIM;
+    const size_t kv_row = (size_t)a.Hk * HEAD_DIM;
+    u32x4 kreg[CPT], vreg[CPT];
+    int4 dreg = {0, 0, 0, 0};
+    int nkey0 = 0;
+    bool nmask = false;
+
+#define DQ_LOAD_TILE(t)                                                                        \
+    {                                                                                          \
+        const int e_ = a.ent[lb + (t) / TPE];                                                  \
+        bool full_;                                                                            \
+        if constexpr (SPARSE) {                                                                \
+            nkey0 = e_ * a.sblock + ((t) % TPE) * FWD_BN;                                      \
+            full_ = true;                                                                      \
+        } else {                                                                               \
+            nkey0 = (e_ >> 1) * FWD_BN;                                                        \
+            full_ = (e_ & 1) != 0;                                                             \
+        }                                                                                      \
+        nmask = !full_ || nkey0 + FWD_BN > T;                                                  \
+        _Pragma("unroll") for (int i = 0; i < CPT; ++i) {                                      \
+            const int c_ = tid + i * NT, key_ = nkey0 + (c_ >> 4);                             \
+            const size_t o_ = (size_t)key_ * kv_row + (c_ & 15) * 8;                           \
+            u32x4 x_ = {0u, 0u, 0u, 0u}, z_ = {0u, 0u, 0u, 0u};                                \
+            if (key_ < T) {                                                                    \
+                x_ = *reinterpret_cast<const u32x4*>(kbase + o_);                              \
+                z_ = *reinterpret_cast<const u32x4*>(vbase + o_);                              \
+            }                                                                                  \
+            kreg[i] = x_;                                                                      \
+            vreg[i] = z_;                                                                      \
+        }                                                                                      \
+        if (!SPARSE && nmask && tid < FWD_BN) {                                                \
+            const int key_ = nkey0 + tid;                                                      \
+            dreg = key_ < T ? a.desc[key_] : int4{0, 0, 0, 0};                                 \
+        }                                                                                      \
+    }
+
+    if (ntiles > 0) DQ_LOAD_TILE(0);
+
+    for (int t = 0; t < ntiles; ++t) {
+        const int key0 = nkey0;
+        const bool need_mask = nmask;
+
+        lds_barrier();   // every wave is done reading the previous tile
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = tid + i * NT, row = c >> 4, d0 = (c & 15) * 8;
+            *reinterpret_cast<u32x4*>(&Kh[swz_off(row, d0)]) = bf16x8_to_f16x8_scaled(kreg[i], sK);
+            *reinterpret_cast<u32x4*>(&Vh[swz_off(row, d0)]) = bf16x8_to_f16x8_scaled(vreg[i], sV);
+        }
+        if (!SPARSE && need_mask && tid < FWD_BN) Ds[tid] = dreg;
+        lds_barrier();
+
+        if (t + 1 < ntiles) DQ_LOAD_TILE(t + 1);
+
+        // per 32-key half kb: S^T = K Q^T and dP^T = V dO^T (lane column = its query row,
+        // rows = keys), dS^T, then dQ^T += (K * sK)^T (dS^T * sO) for those 32 keys
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            f32x16 st, dpt;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                st[r] = 0.f;
+                dpt[r] = 0.f;
+            }
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                const int off = swz_off(kb * 32 + l32, 16 * ks + 8 * hf);
+                st = mfma32h(*reinterpret_cast<const f16x8*>(&Kh[off]), qf[ks], st);
+                dpt = mfma32h(*reinterpret_cast<const f16x8*>(&Vh[off]), df[ks], dpt);
+            }
+            // dS^T * sO = P^T * (dP^T * sO - D * sO), as B operands of two 16-key steps;
+            // key slot (hf, e) of step kk is key kb*32 + 16*kk + 8*(e/4) + 4*hf + e%4
+            f16x8 sb[2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                u32x4 pk;
+#pragma unroll
+                for (int e2 = 0; e2 < 8; e2 += 2) {
+                    float v2[2];
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const int r = kk * 8 + e2 + j;
+                        const int kidx = kb * 32 + acc_row(r, hf);
+                        bool vis = true;
+                        if (need_mask) {
+                            if constexpr (SPARSE) {
+                                vis = key0 + kidx < T;
+                            } else {
+                                const int4 d = Ds[kidx];
+                                vis = (pos >= d.x && pos < d.y) || (pos >= d.z && pos < d.w);
+                            }
+                        }
+                        const float p = vis ? fast_exp2(fmaf(st[r], cS, -lse2)) : 0.f;
+                        v2[j] = p * fmaf(dpt[r], inv_sV, -dd);
+                    }
+                    pk[e2 >> 1] = pack_f16(v2[0], v2[1]);
+                }
+                sb[kk] = as_f16x8(pk);
+            }
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const int k0 = kb * 32 + 16 * kk + 4 * hf;
+                    acc[db] = mfma32h(tr_operand_swz(Kh, k0, k0 + 8, db * 32, lane), sb[kk], acc[db]);
+                }
+        }
+    }
+#undef DQ_LOAD_TILE
+
+    if (row_ok) {
+        const float unscale = a.scale / (sO * sK);
+        float* op = a.dq + ((size_t)pos * a.Hq + head) * HEAD_DIM;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const int d0 = db * 32 + 8 * i4 + 4 * hf;
+                *reinterpret_cast<float4*>(op + d0) =
+                    float4{acc[db][4 * i4] * unscale, acc[db][4 * i4 + 1] * unscale,
+                           acc[db][4 * i4 + 2] * unscale, acc[db][4 * i4 + 3] * unscale};
+            }
+    }
+}
+
 hipError_t launch_bwd_pre(const Problem& P, const void* q, const void* k, const void* v, const void* o,
-                          const void* o_lo, const void* dout, float* dq, float* dbuf, hipStream_t s) {
+                          const void* o_lo, const void* dout, float* dbuf, hipStream_t s) {
     float* stats = reinterpret_cast<float*>(reinterpret_cast<char*>(dbuf) + bwd_stats_offset(P.Hq, P.T));
-    const size_t n4 = (size_t)P.T * P.Hq * HEAD_DIM / 4;
-    hipLaunchKernelGGL(zero_kernel, dim3(2048), dim3(256), 0, s, reinterpret_cast<float4*>(dq), n4, stats);
+    hipLaunchKernelGGL(zero_stats_kernel, dim3(1), dim3(64), 0, s, stats);
     const long rows = (long)P.T * P.Hq;
     hipLaunchKernelGGL(bwd_pre_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s,
                        static_cast<const bf16*>(o), static_cast<const bf16*>(o_lo), static_cast<const bf16*>(dout),
@@ -598,6 +737,22 @@ hipError_t launch_bwd_main(const Problem& P, const void* q, const void* k, const
         hipLaunchKernelGGL((bwd_kernel<2, true>), dim3(P.Hk * P.nb), dim3(256), 0, s, a);
     } else {
         hipLaunchKernelGGL((bwd_kernel<4, true>), dim3(P.Hk * P.nb), dim3(512), 0, s, a);
+    }
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+
+    // dQ pass on the forward's lists
+    BwdArgs b = a;
+    b.ptr = reinterpret_cast<const int*>(base + L.fwd_ptr);
+    b.ent = reinterpret_cast<const int*>(base + L.fwd_ent);
+    b.order = P.sparse ? nullptr : reinterpret_cast<const int*>(base + L.fwd_order);
+    b.BMq = P.fBM;
+    if (!P.sparse) {
+        hipLaunchKernelGGL((dq_kernel<8, false>), dim3(P.Hk * P.nqt_f), dim3(512), 0, s, b);
+    } else if (P.sblock == 64) {
+        hipLaunchKernelGGL((dq_kernel<2, true>), dim3(P.Hk * P.G * P.nb), dim3(128), 0, s, b);
+    } else {
+        hipLaunchKernelGGL((dq_kernel<4, true>), dim3(P.Hk * P.G * P.nb), dim3(256), 0, s, b);
     }
     return hipGetLastError();
 }

@@ -120,7 +120,7 @@ hipError_t launch_index_sparse(const Problem& P, const uint8_t* keep, void* inde
 hipError_t launch_fwd(const Problem& P, const void* q, const void* k, const void* v, void* o, void* o_lo,
                       float* lse, const int4* desc, const void* index, hipStream_t s);
 hipError_t launch_bwd_pre(const Problem& P, const void* q, const void* k, const void* v, const void* o,
-                          const void* o_lo, const void* dout, float* dq, float* dbuf, hipStream_t s);
+                          const void* o_lo, const void* dout, float* dbuf, hipStream_t s);
 hipError_t launch_bwd_main(const Problem& P, const void* q, const void* k, const void* v, const float* lse,
                            const void* dout, float* dq, float* dk, float* dv, const int4* desc,
                            const void* index, const float* dbuf, hipStream_t s);

@@ -75,8 +75,8 @@ def test_entry_points_reject_before_launch():
     sp = attn.problem(1024, 8, 2, "block_sparse", 64)
     assert L.attn_tile_index_build(ctypes.byref(sp), fake, fake, attn.tile_index_size(sp), None) == attn.ATTN_ERR_INVALID_ARG
     assert L.attn_query_tile_shape(ctypes.byref(sp), *([ctypes.byref(ctypes.c_int32())] * 4)) == attn.ATTN_ERR_INVALID_ARG
-    assert L.attn_bwd_preprocess(ctypes.byref(p), fake, fake, fake, fake, None, fake, fake, fake, ws - 1, None) == attn.ATTN_ERR_WORKSPACE
-    assert L.attn_bwd_preprocess(ctypes.byref(p), None, fake, fake, fake, None, fake, fake, fake, ws, None) == attn.ATTN_ERR_INVALID_ARG
+    assert L.attn_bwd_preprocess(ctypes.byref(p), fake, fake, fake, fake, None, fake, fake, ws - 1, None) == attn.ATTN_ERR_WORKSPACE
+    assert L.attn_bwd_preprocess(ctypes.byref(p), None, fake, fake, fake, None, fake, fake, ws, None) == attn.ATTN_ERR_INVALID_ARG
     assert L.attn_bwd_main(ctypes.byref(p), *([fake] * 9), fake, need, fake, ws - 1, None) == attn.ATTN_ERR_WORKSPACE
     assert L.attn_cast_bf16(None, fake, 10, None) == attn.ATTN_ERR_INVALID_ARG
     assert L.attn_cast_bf16(None, None, 0, None) == attn.ATTN_OK
