@@ -4,7 +4,8 @@
 One step = one pass of the whole path over one batch of synthetic inputs that are
 already resident in HBM:
   column-interval descriptor (host) -> device copy -> tile index (classifier + lists)
-  -> attn_fwd -> attn_bwd_preprocess (D = rowsum(dO*O), operand bounds) -> attn_bwd_main.
+  -> attn_fwd -> attn_bwd_preprocess (D = rowsum(dO*O), operand bounds)
+  -> attn_bwd_dkdv (dK, dV) -> attn_bwd_dq (dQ).
 The default workload is CAUSAL at T = 8192, 64 query heads sharing 8 KV heads, head
 dim 128, bf16 inputs N(0,1) from a seed.
 
@@ -114,6 +115,9 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=2, help="query heads in the oracle timing sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--out", default=None, help="also append the JSON line to this file")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run attn_cast_bf16 over 2^28 floats 5 times (reads 1 GiB, writes 512 MiB "
+                         "per launch): the known-size kernel that scales the HBM byte counters")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -128,6 +132,17 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     attn.lib()   # fail loudly if the HIP library is missing
+
+    if args.copy_calibration:
+        n = 1 << 28
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty(n, dtype=torch.bfloat16, device=dev)
+        for _ in range(5):
+            attn.cast_bf16(src.data_ptr(), dst.data_ptr(), n, torch.cuda.current_stream(dev).cuda_stream)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration": {"kernel": "cast_kernel", "launches": 5,
+                                               "read_bytes": 4 * n, "write_bytes": 2 * n}}))
+        return
 
     wl = workloads(args.seed)[args.workload]
     T, Hq, Hk, d, spec = wl.T, wl.Hq, wl.Hk, wl.d, wl.mask
@@ -162,8 +177,8 @@ def main():
     fwd_flops = 4.0 * d * (U_all if U_all is not None else Hq * U)
     bwd_flops = 2.5 * fwd_flops
 
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
-    times = {"index": [], "fwd": [], "bwd_pre": [], "bwd_main": []}
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    times = {"index": [], "fwd": [], "bwd_pre": [], "bwd_dkdv": [], "bwd_dq": []}
 
     def step(record: bool):
         if sparse:
@@ -181,16 +196,21 @@ def main():
         attn.bwd_preprocess(prob, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), o_lo.data_ptr(),
                             do.data_ptr(), ws.data_ptr(), ws_bytes, sp)                                     # a4
         ev[3].record(stream)
-        attn.bwd_main(prob, q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(), do.data_ptr(),
-                      dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), 0 if sparse else desc_dev.data_ptr(),
-                      index.data_ptr(), idx_bytes, ws.data_ptr(), ws_bytes, sp)                     # a5
+        attn.bwd_dkdv(prob, q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                      dk.data_ptr(), dv.data_ptr(), 0 if sparse else desc_dev.data_ptr(),
+                      index.data_ptr(), idx_bytes, ws.data_ptr(), ws_bytes, sp)                     # a5 (dK, dV)
         ev[4].record(stream)
+        attn.bwd_dq(prob, q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(), do.data_ptr(),
+                    dq.data_ptr(), 0 if sparse else desc_dev.data_ptr(),
+                    index.data_ptr(), idx_bytes, ws.data_ptr(), ws_bytes, sp)                       # a5 (dQ)
+        ev[5].record(stream)
         if record:
-            ev[4].synchronize()
+            ev[5].synchronize()
             times["index"].append(ev[0].elapsed_time(ev[1]))
             times["fwd"].append(ev[1].elapsed_time(ev[2]))
             times["bwd_pre"].append(ev[2].elapsed_time(ev[3]))
-            times["bwd_main"].append(ev[3].elapsed_time(ev[4]))
+            times["bwd_dkdv"].append(ev[3].elapsed_time(ev[4]))
+            times["bwd_dq"].append(ev[4].elapsed_time(ev[5]))
 
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -213,14 +233,17 @@ def main():
     torch.cuda.synchronize()
     med = {k: float(np.median(v)) for k, v in times.items()}
     mean = {k: float(np.mean(v)) for k, v in times.items()}
-    t_bwd = med["bwd_pre"] + med["bwd_main"]
+    t_bwd = med["bwd_pre"] + med["bwd_dkdv"] + med["bwd_dq"]
     fwd_tf = fwd_flops / (med["fwd"] * 1e-3) / 1e12
     bwd_tf = bwd_flops / (t_bwd * 1e-3) / 1e12
-    main_tf = bwd_flops / (mean["bwd_main"] * 1e-3) / 1e12
+    # dominant kernel: bwd_kernel (attn_bwd_dkdv), algorithmic work = the S, dP, dV and dK
+    # products over the visible pairs = 8 * d * Hq * U
+    dkdv_flops = 0.8 * bwd_flops
+    dkdv_tf = dkdv_flops / (mean["bwd_dkdv"] * 1e-3) / 1e12
     value = (fwd_flops + bwd_flops) / (ms_per_step * 1e-3) / 1e12
     log(f"step {ms_per_step:.3f} ms | index {med['index']:.3f} fwd {med['fwd']:.3f} "
-        f"bwd_pre {med['bwd_pre']:.3f} bwd_main {med['bwd_main']:.3f} ms | fwd {fwd_tf:.1f} TF/s "
-        f"bwd {bwd_tf:.1f} TF/s")
+        f"bwd_pre {med['bwd_pre']:.3f} dkdv {med['bwd_dkdv']:.3f} dq {med['bwd_dq']:.3f} ms | "
+        f"fwd {fwd_tf:.1f} TF/s bwd {bwd_tf:.1f} TF/s")
 
     rec = {
         "metric": METRIC,
@@ -242,14 +265,15 @@ def main():
                 "frac_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4)},
         "bwd": {"ms": round(t_bwd, 4), "tflops": round(bwd_tf, 2),
                 "frac_peak": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
-                "preprocess_ms": round(med["bwd_pre"], 4), "main_ms": round(med["bwd_main"], 4)},
+                "preprocess_ms": round(med["bwd_pre"], 4), "dkdv_ms": round(med["bwd_dkdv"], 4),
+                "dq_ms": round(med["bwd_dq"], 4)},
         "index_build_ms": round(med["index"], 4),
-        "roofline": {"kernel": "bwd_kernel (attn_bwd_main)", "bound": "mfma",
-                     "achieved": round(main_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(main_tf / PEAK_BF16_TFLOPS, 4),
+        "roofline": {"kernel": "bwd_kernel (attn_bwd_dkdv)", "bound": "mfma",
+                     "achieved": round(dkdv_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(dkdv_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_for(wl.name, "bwd_kernel"),
-                     "avg_launch_ms": round(mean["bwd_main"], 4),
-                     "flops_per_launch": bwd_flops},
+                     "avg_launch_ms": round(mean["bwd_dkdv"], 4),
+                     "flops_per_launch": dkdv_flops},
         "kernel_hash": kernel_hash(),
     }
     if not args.no_cpu_baseline:

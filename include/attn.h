@@ -240,6 +240,18 @@ attn_status attn_bwd_main(const attn_problem* prob, const void* q, const void* k
                           const void* index_dev, size_t index_bytes,
                           const void* ws, size_t ws_bytes, void* stream);
 
+/* The two halves of attn_bwd_main, for callers that time or schedule them apart:
+ * attn_bwd_dkdv writes dK and dV (key-tile major), attn_bwd_dq writes dQ (query-tile
+ * major). Both read only the inputs, the forward's LSE and the preprocessed workspace. */
+attn_status attn_bwd_dkdv(const attn_problem* prob, const void* q, const void* k, const void* v,
+                          const float* lse, const void* dout, float* dk, float* dv,
+                          const int32_t* desc_dev, const void* index_dev, size_t index_bytes,
+                          const void* ws, size_t ws_bytes, void* stream);
+attn_status attn_bwd_dq(const attn_problem* prob, const void* q, const void* k, const void* v,
+                        const float* lse, const void* dout, float* dq,
+                        const int32_t* desc_dev, const void* index_dev, size_t index_bytes,
+                        const void* ws, size_t ws_bytes, void* stream);
+
 /* Optional cast of fp32 gradients to bf16 (round to nearest even): out[i] = bf16(in[i]). */
 attn_status attn_cast_bf16(const float* in, void* out, size_t n, void* stream);
 

@@ -88,6 +88,8 @@ _SIGS = {
     "attn_bwd": (ctypes.c_int, [_PROB, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _SZ, _P]),
     "attn_bwd_preprocess": (ctypes.c_int, [_PROB, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "attn_bwd_main": (ctypes.c_int, [_PROB, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _SZ, _P]),
+    "attn_bwd_dkdv": (ctypes.c_int, [_PROB, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _SZ, _P]),
+    "attn_bwd_dq": (ctypes.c_int, [_PROB, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _SZ, _P]),
     "attn_cast_bf16": (ctypes.c_int, [_P, _P, _SZ, _P]),
 }
 
@@ -216,6 +218,16 @@ def bwd_preprocess(prob, q, k, v, o, o_lo, dout, ws, ws_bytes, stream=0):
 def bwd_main(prob, q, k, v, lse, dout, dq, dk, dv, desc, index, index_bytes, ws, ws_bytes, stream=0):
     _check(lib().attn_bwd_main(ctypes.byref(prob), q, k, v, lse, dout, dq, dk, dv, desc, index, index_bytes,
                                ws, ws_bytes, stream), "attn_bwd_main")
+
+
+def bwd_dkdv(prob, q, k, v, lse, dout, dk, dv, desc, index, index_bytes, ws, ws_bytes, stream=0):
+    _check(lib().attn_bwd_dkdv(ctypes.byref(prob), q, k, v, lse, dout, dk, dv, desc, index, index_bytes,
+                               ws, ws_bytes, stream), "attn_bwd_dkdv")
+
+
+def bwd_dq(prob, q, k, v, lse, dout, dq, desc, index, index_bytes, ws, ws_bytes, stream=0):
+    _check(lib().attn_bwd_dq(ctypes.byref(prob), q, k, v, lse, dout, dq, desc, index, index_bytes,
+                             ws, ws_bytes, stream), "attn_bwd_dq")
 
 
 def cast_bf16(src: int, dst: int, n: int, stream: int = 0):

@@ -345,19 +345,43 @@ attn_status attn_bwd_preprocess(const attn_problem* prob, const void* q, const v
     return hip_status(launch_bwd_pre(P, q, k, v, o, o_lo, dout, (float*)ws, (hipStream_t)stream));
 }
 
-attn_status attn_bwd_main(const attn_problem* prob, const void* q, const void* k, const void* v,
-                          const float* lse, const void* dout, float* dq, float* dk, float* dv,
-                          const int32_t* desc_dev, const void* index_dev, size_t index_bytes, const void* ws,
-                          size_t ws_bytes, void* stream) {
+static attn_status bwd_parts(const attn_problem* prob, const void* q, const void* k, const void* v,
+                             const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                             const int32_t* desc_dev, const void* index_dev, size_t index_bytes, const void* ws,
+                             size_t ws_bytes, void* stream, int parts) {
     Problem P;
     attn_status st = validate_problem(prob, &P);
     if (st != ATTN_OK) return st;
-    if (!q || !k || !v || !lse || !dout || !dq || !dk || !dv || !index_dev) return ATTN_ERR_INVALID_ARG;
+    if (!q || !k || !v || !lse || !dout || !index_dev) return ATTN_ERR_INVALID_ARG;
+    if (((parts & BWD_PART_DQ) && !dq) || ((parts & BWD_PART_DKDV) && (!dk || !dv))) return ATTN_ERR_INVALID_ARG;
     if (!P.sparse && !desc_dev) return ATTN_ERR_INVALID_ARG;
     if (index_bytes < index_layout(P).total) return ATTN_ERR_WORKSPACE;
     if ((st = check_bwd_ws(prob, ws, ws_bytes)) != ATTN_OK) return st;
     return hip_status(launch_bwd_main(P, q, k, v, lse, dout, dq, dk, dv, reinterpret_cast<const int4*>(desc_dev),
-                                      index_dev, (const float*)ws, (hipStream_t)stream));
+                                      index_dev, (const float*)ws, parts, (hipStream_t)stream));
+}
+
+attn_status attn_bwd_main(const attn_problem* prob, const void* q, const void* k, const void* v,
+                          const float* lse, const void* dout, float* dq, float* dk, float* dv,
+                          const int32_t* desc_dev, const void* index_dev, size_t index_bytes, const void* ws,
+                          size_t ws_bytes, void* stream) {
+    return bwd_parts(prob, q, k, v, lse, dout, dq, dk, dv, desc_dev, index_dev, index_bytes, ws, ws_bytes, stream,
+                     BWD_PART_DKDV | BWD_PART_DQ);
+}
+
+attn_status attn_bwd_dkdv(const attn_problem* prob, const void* q, const void* k, const void* v,
+                          const float* lse, const void* dout, float* dk, float* dv, const int32_t* desc_dev,
+                          const void* index_dev, size_t index_bytes, const void* ws, size_t ws_bytes,
+                          void* stream) {
+    return bwd_parts(prob, q, k, v, lse, dout, nullptr, dk, dv, desc_dev, index_dev, index_bytes, ws, ws_bytes,
+                     stream, BWD_PART_DKDV);
+}
+
+attn_status attn_bwd_dq(const attn_problem* prob, const void* q, const void* k, const void* v,
+                        const float* lse, const void* dout, float* dq, const int32_t* desc_dev,
+                        const void* index_dev, size_t index_bytes, const void* ws, size_t ws_bytes, void* stream) {
+    return bwd_parts(prob, q, k, v, lse, dout, dq, nullptr, nullptr, desc_dev, index_dev, index_bytes, ws, ws_bytes,
+                     stream, BWD_PART_DQ);
 }
 
 attn_status attn_bwd(const attn_problem* prob, const void* q, const void* k, const void* v, const void* o,

@@ -703,7 +703,7 @@ hipError_t launch_bwd_pre(const Problem& P, const void* q, const void* k, const 
 
 hipError_t launch_bwd_main(const Problem& P, const void* q, const void* k, const void* v, const float* lse,
                            const void* dout, float* dq, float* dk, float* dv, const int4* desc,
-                           const void* index, const float* dbuf, hipStream_t s) {
+                           const void* index, const float* dbuf, int parts, hipStream_t s) {
     const IndexLayout L = index_layout(P);
     const char* base = static_cast<const char*>(index);
     BwdArgs a;
@@ -731,15 +731,18 @@ hipError_t launch_bwd_main(const Problem& P, const void* q, const void* k, const
     a.sblock = P.sblock;
     a.c = P.scale * LOG2E;
     a.scale = P.scale;
-    if (!P.sparse) {
-        hipLaunchKernelGGL((bwd_kernel<4, false>), dim3(P.Hk * P.nkt_b), dim3(512), 0, s, a);
-    } else if (P.sblock == 64) {
-        hipLaunchKernelGGL((bwd_kernel<2, true>), dim3(P.Hk * P.nb), dim3(256), 0, s, a);
-    } else {
-        hipLaunchKernelGGL((bwd_kernel<4, true>), dim3(P.Hk * P.nb), dim3(512), 0, s, a);
+    if (parts & BWD_PART_DKDV) {
+        if (!P.sparse) {
+            hipLaunchKernelGGL((bwd_kernel<4, false>), dim3(P.Hk * P.nkt_b), dim3(512), 0, s, a);
+        } else if (P.sblock == 64) {
+            hipLaunchKernelGGL((bwd_kernel<2, true>), dim3(P.Hk * P.nb), dim3(256), 0, s, a);
+        } else {
+            hipLaunchKernelGGL((bwd_kernel<4, true>), dim3(P.Hk * P.nb), dim3(512), 0, s, a);
+        }
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
     }
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
+    if (!(parts & BWD_PART_DQ)) return hipSuccess;
 
     // dQ pass on the forward's lists
     BwdArgs b = a;

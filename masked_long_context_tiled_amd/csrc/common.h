@@ -121,9 +121,10 @@ hipError_t launch_fwd(const Problem& P, const void* q, const void* k, const void
                       float* lse, const int4* desc, const void* index, hipStream_t s);
 hipError_t launch_bwd_pre(const Problem& P, const void* q, const void* k, const void* v, const void* o,
                           const void* o_lo, const void* dout, float* dbuf, hipStream_t s);
+enum { BWD_PART_DKDV = 1, BWD_PART_DQ = 2 };
 hipError_t launch_bwd_main(const Problem& P, const void* q, const void* k, const void* v, const float* lse,
                            const void* dout, float* dq, float* dk, float* dv, const int4* desc,
-                           const void* index, const float* dbuf, hipStream_t s);
+                           const void* index, const float* dbuf, int parts, hipStream_t s);
 hipError_t launch_cast_bf16(const float* in, void* out, size_t n, hipStream_t s);
 
 }  // namespace mlct

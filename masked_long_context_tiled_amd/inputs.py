@@ -83,10 +83,13 @@ class MaskSpec:
 # ---------------------------------------------------------------------------
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """Round float32 values to bf16 (round to nearest, ties to even); return uint16 bits."""
+    """Round finite float32 values to bf16 (round to nearest, ties to even); return uint16 bits.
+
+    For finite inputs the 32-bit sum below cannot overflow (the largest, 0xFF7FFFFF + 0x8000,
+    stays below 2^32)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    b = x.view(np.uint32).astype(np.uint64)
-    rounded = (b + 0x7FFF + ((b >> 16) & 1)) >> 16
+    b = x.view(np.uint32)
+    rounded = (b + np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
     return rounded.astype(np.uint16)
 
 

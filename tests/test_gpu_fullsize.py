@@ -1,0 +1,154 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration bench.py times.
+
+The whole forward and backward run on the GPU at full size; the fp64 oracle then checks
+  * O, LSE and dQ on sampled rows (every row of the oracle is exact on its own), and
+  * dK, dV on key-column slabs whose visible rows are few enough to compute in full,
+  * elsewhere the gradient identities that hold at any size: sum_j dK_j = 0 per KV
+    head and sum_j dV_j = sum of dO over the group's rows that see a key.
+Bounds as in the small cases: max |err| <= 2e-2 on O, dQ, dK, dV; LSE within 1e-3.
+"""
+import numpy as np
+import pytest
+
+from masked_long_context_tiled_amd import attn
+from masked_long_context_tiled_amd.inputs import attention_inputs, bf16_bits_to_f64, keep_for, workloads
+from oracle.attention import attention_backward
+from oracle.masks import mask_block
+
+from gpu_helpers import LSE_TOL, TOL, assert_close, bf16_dev_to_f64, note, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(name, seed=0):
+    import torch
+    wl = workloads(seed)[name]
+    note(f"full size {name}: T={wl.T} Hq={wl.Hq} Hk={wl.Hk} mask={wl.mask.kind}: inputs")
+    x = attention_inputs(seed, wl.T, wl.Hq, wl.Hk)
+    keep = keep_for(wl, seed)
+    q, k, v, do = (to_dev_bf16(x[n], torch) for n in ("q", "k", "v", "do"))
+    note(f"full size {name}: GPU forward + backward")
+    ma = attn.MaskedAttention(wl.T, wl.Hq, wl.Hk, wl.mask, keep=keep)
+    o, lse, o_lo = ma.forward(q, k, v)
+    dq, dk, dv = ma.backward(q, k, v, o, lse, do, o_lo=o_lo)
+    torch.cuda.synchronize()
+    return wl, x, keep, {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
+
+
+def _group_arrays(x, wl, heads):
+    """fp64 inputs restricted to query heads `heads` (all in one KV group) and their KV head."""
+    G = wl.Hq // wl.Hk
+    g = heads[0] // G
+    assert all(h // G == g for h in heads)
+    sub = lambda a, hs: bf16_bits_to_f64(np.ascontiguousarray(a[:, hs]))
+    return sub(x["q"], heads), sub(x["k"], [g]), sub(x["v"], [g]), sub(x["do"], heads), g
+
+
+def _check_rows(wl, x, keep, out, heads, rows):
+    G = wl.Hq // wl.Hk
+    groups = sorted({h // G for h in heads})
+    if len(groups) > 1:                       # one oracle call per KV group
+        for g in groups:
+            _check_rows(wl, x, keep, out, [h for h in heads if h // G == g], rows)
+        return
+    import torch
+    q, k, v, do, g = _group_arrays(x, wl, heads)
+    kp = None if keep is None else keep[heads]
+    ref = attention_backward(q, k, v, do, wl.mask, rows=rows, keep=kp)
+    r_t = torch.as_tensor(rows, device=out["dq"].device)
+    h_t = torch.as_tensor(heads, device=out["dq"].device)
+    o = bf16_dev_to_f64(out["o"][r_t][:, h_t].contiguous())
+    lse = out["lse"][h_t][:, r_t].cpu().numpy()
+    dq = out["dq"][r_t][:, h_t].cpu().numpy()
+    e = (assert_close("O", o, ref["o"], TOL), assert_close("LSE", lse, ref["lse"], LSE_TOL),
+         assert_close("dQ", dq, ref["dq"], TOL))
+    note(f"  rows {len(rows)} heads {heads}: O {e[0]:.2e} LSE {e[1]:.2e} dQ {e[2]:.2e}")
+
+
+def _check_key_slab(wl, x, keep, out, g, cols):
+    """dK, dV of KV head g on key columns `cols`, from every row that sees one of them."""
+    G = wl.Hq // wl.Hk
+    heads = list(range(g * G, (g + 1) * G))
+    q, k, v, do, _ = _group_arrays(x, wl, heads)
+    kp = None if keep is None else keep[heads]
+    seen = np.zeros(wl.T, dtype=bool)
+    for hi in range(G):
+        for r0 in range(0, wl.T, 4096):
+            rr = np.arange(r0, min(wl.T, r0 + 4096))
+            seen[rr] |= mask_block(wl.mask, wl.T, rr, cols, hi, kp).any(axis=1)
+    rows = np.nonzero(seen)[0]
+    ref = attention_backward(q, k, v, do, wl.mask, rows=rows, key_cols=cols, keep=kp)
+    dk = out["dk"][cols.min():cols.max() + 1, g].cpu().numpy()[cols - cols.min()]
+    dv = out["dv"][cols.min():cols.max() + 1, g].cpu().numpy()[cols - cols.min()]
+    e = (assert_close("dK", dk, ref["dk"][:, 0], TOL), assert_close("dV", dv, ref["dv"][:, 0], TOL))
+    note(f"  key slab [{cols.min()}, {cols.max()}] of KV head {g} ({len(rows)} rows): dK {e[0]:.2e} dV {e[1]:.2e}")
+
+
+def _check_sums(wl, x, out, rows_visible=None):
+    """sum_j dK_j = 0 and sum_j dV_j = sum over rows with a visible key of dO, per KV head."""
+    import torch
+    G = wl.Hq // wl.Hk
+    dk_sum = out["dk"].double().sum(0).cpu().numpy()               # [Hk][d]
+    dv_sum = out["dv"].double().sum(0).cpu().numpy()
+    do = torch.from_numpy(np.ascontiguousarray(x["do"]).view(np.int16)).view(torch.bfloat16)
+    finite = torch.isfinite(out["lse"]).cpu()                       # [Hq][T]
+    want = np.zeros((wl.Hk, 128))
+    for h in range(wl.Hq):
+        want[h // G] += (do[:, h].double() * finite[h][:, None]).sum(0).numpy()
+    # each sum adds T * G terms of size ~1 whose P and dS carry independent fp16 rounding
+    # (relative 2^-12): the error grows like the square root of the number of terms; a
+    # missing or doubled tile would be off by far more
+    tol = 5e-2 * np.sqrt(wl.T * G / 512.0)
+    e1 = assert_close("sum dK", dk_sum, 0.0 * dk_sum, tol)
+    e2 = assert_close("sum dV", dv_sum, want, tol)
+    note(f"  gradient sums: |sum dK| {e1:.2e}  |sum dV - sum dO| {e2:.2e}  (bound {tol:.2e})")
+
+
+def _sample_rows(T, n, seed):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, 1, T // 2, T - 1], rng.integers(0, T, n)]))
+
+
+@pytest.mark.parametrize("name", ["causal_8k_gqa", "full_8k_gqa", "causal_8k_mha", "full_8k_mha"])
+def test_8k(name):
+    wl, x, keep, out = _run(name)
+    G = wl.Hq // wl.Hk
+    _check_rows(wl, x, keep, out, heads=[0, 1], rows=_sample_rows(wl.T, 48, 1))
+    _check_rows(wl, x, keep, out, heads=[wl.Hq - G], rows=_sample_rows(wl.T, 48, 2))
+    last = wl.Hk - 1
+    _check_key_slab(wl, x, keep, out, last, np.arange(wl.T - 96, wl.T))
+    if wl.mask.kind == "causal" and G == 8:
+        _check_key_slab(wl, x, keep, out, 3, np.arange(6144, 6208))
+    _check_sums(wl, x, out)
+
+
+@pytest.mark.parametrize("name", ["full_document_32k", "causal_document_32k", "full_sliding_window_32k",
+                                  "causal_sliding_window_32k", "shared_question_16k", "prefix_lm_causal_16k",
+                                  "causal_blockwise_16k", "global_sliding_16k"])
+def test_workload_masks(name):
+    wl, x, keep, out = _run(name)
+    _check_rows(wl, x, keep, out, heads=[8, 15], rows=_sample_rows(wl.T, 24, 3))
+    kind = wl.mask.kind
+    if kind in ("causal_document", "full_document"):
+        cu = np.asarray(wl.mask.cu_seqlens)
+        d = int(np.argmin(np.diff(cu)))                        # the shortest document
+        _check_key_slab(wl, x, keep, out, 5, np.arange(cu[d], min(cu[d + 1], cu[d] + 64)))
+    elif kind in ("causal_sliding_window", "shared_question", "prefix_lm_causal", "causal_blockwise"):
+        _check_key_slab(wl, x, keep, out, 2, np.arange(wl.T - 64, wl.T))
+    _check_sums(wl, x, out)
+
+
+@pytest.mark.timeout(900)
+def test_causal_128k():
+    wl, x, keep, out = _run("causal_128k")
+    _check_rows(wl, x, keep, out, heads=[0, 5], rows=_sample_rows(wl.T, 12, 4))
+    _check_key_slab(wl, x, keep, out, 7, np.arange(wl.T - 48, wl.T))
+    _check_sums(wl, x, out)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["block_sparse_64k_b128", "block_sparse_64k_b64"])
+def test_block_sparse_64k(name):
+    wl, x, keep, out = _run(name)
+    _check_rows(wl, x, keep, out, heads=[16, 17], rows=_sample_rows(wl.T, 12, 5))
+    _check_sums(wl, x, out)
