@@ -309,7 +309,7 @@ attn_status attn_bwd_workspace_size(const attn_problem* prob, size_t* bytes_out)
     attn_status st = validate_problem(prob, &P);
     if (st != ATTN_OK) return st;
     if (!bytes_out) return ATTN_ERR_INVALID_ARG;
-    *bytes_out = bwd_workspace_bytes(P.Hq, P.T);   // D = rowsum(dO * O) [Hq][T] + operand bounds
+    *bytes_out = bwd_layout(P.Hq, P.Hk, P.T).total;   // D, operand bounds, scaled fp16 Q, dO, K, V
     return ATTN_OK;
 }
 

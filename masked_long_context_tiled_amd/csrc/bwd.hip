@@ -41,6 +41,10 @@ struct BwdArgs {
     const float* lse;
     const float* dbuf;    // D [Hq][T]
     const float* stats;   // BWD_STATS bounds
+    const _Float16* qh;   // Q * sQ, dO * sO [T][Hq][128], K * sK, V * sV [T][Hk][128] (fp16)
+    const _Float16* doh;
+    const _Float16* kh;
+    const _Float16* vh;
     float* dq;
     float* dk;
     float* dv;
@@ -58,6 +62,22 @@ __device__ __forceinline__ float pow2_scale(float bound) {
     if (!(bound > 0.f) || isinf(bound)) return 1.f;
     const float e = fminf(fmaxf(floorf(__log2f(32768.f / bound)), -120.f), 120.f);
     return exp2f(e);
+}
+
+// The power-of-two scales of the fp16 operands, from the preprocess bounds. dS is bounded
+// by 2 max||dO_i|| max||V_j|| (|P| <= 1, |dP_ij| <= ||dO_i|| ||V_j||, |D_i| <= ||dO_i||), so
+// dO's scale also keeps dS * sO in range.
+struct OperandScales {
+    float sQ, sK, sV, sO;
+};
+__device__ __forceinline__ OperandScales operand_scales(const float* stats) {
+    const float nrm_do = sqrtf(stats[ST_DO_NORM2]), nrm_v = sqrtf(stats[ST_V_NORM2]);
+    OperandScales r;
+    r.sO = pow2_scale(fmaxf(2.f * nrm_do * nrm_v, nrm_do));
+    r.sQ = pow2_scale(stats[ST_Q_ABS]);
+    r.sK = pow2_scale(stats[ST_K_ABS]);
+    r.sV = pow2_scale(nrm_v);
+    return r;
 }
 
 __device__ __forceinline__ float wave_max(float x) {
@@ -152,6 +172,33 @@ __global__ __launch_bounds__(256) void rownorm_kernel(const bf16* __restrict__ p
     block_max_to(out, best);
 }
 
+// 8 bf16 (one 16-byte chunk) -> 8 fp16 scaled by s.
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8_scaled(u32x4 x, float s) {
+    u32x4 r;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) r[m] = pack_f16(bf16_lo(x[m]) * s, bf16_hi(x[m]) * s);
+    return r;
+}
+
+// Q, dO, K, V -> fp16 times their scales, once per backward pass (HBM-bound), so the main
+// kernels stage their operands by plain copies.
+__global__ __launch_bounds__(256) void to_f16_kernel(const u32x4* __restrict__ q, const u32x4* __restrict__ dout,
+                                                     const u32x4* __restrict__ k, const u32x4* __restrict__ v,
+                                                     u32x4* __restrict__ qh, u32x4* __restrict__ doh,
+                                                     u32x4* __restrict__ kh, u32x4* __restrict__ vh, size_t nq8,
+                                                     size_t nk8, const float* __restrict__ stats) {
+    const OperandScales sc = operand_scales(stats);
+    const size_t i0 = (size_t)blockIdx.x * blockDim.x + threadIdx.x, stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = i0; i < nq8; i += stride) {
+        qh[i] = bf16x8_to_f16x8_scaled(q[i], sc.sQ);
+        doh[i] = bf16x8_to_f16x8_scaled(dout[i], sc.sO);
+    }
+    for (size_t i = i0; i < nk8; i += stride) {
+        kh[i] = bf16x8_to_f16x8_scaled(k[i], sc.sK);
+        vh[i] = bf16x8_to_f16x8_scaled(v[i], sc.sV);
+    }
+}
+
 __global__ void cast_kernel(const float* __restrict__ in, uint16_t* __restrict__ out, size_t n) {
     const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     const size_t stride = (size_t)gridDim.x * blockDim.x;
@@ -187,80 +234,90 @@ __device__ __forceinline__ RowMap row_map(const BwdArgs& a, int g, int e) {
     return m;
 }
 
-// Transposed LDS read (ds_read_b64_tr_b16): within each group of 16 lanes, source lane s
-// supplies the address of 4 consecutive 16-bit elements and output lane i receives
-// element i % 4 of source lanes i/4, i/4 + 4, i/4 + 8, i/4 + 12. With source lane s
-// pointing at M[r0 + s/4][c0 + 4*(s%4)], output lane i gets M[r0 .. r0+3][c0 + i].
-__device__ __forceinline__ u32x2 ds_read_tr16(const _Float16* p) {
-    typedef short i16x4 __attribute__((ext_vector_type(4)));
-    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
-    return __builtin_bit_cast(u32x2, v);
-}
+// List entries of a work item, 64 per register: lane i of chunk register c holds entry
+// 64 c + i. Entries are read in non-decreasing order; the chunk after the current one is
+// loaded a whole chunk ahead and only touched (waited for) when the reader moves on to it.
+struct EntryStream {
+    const int* ent;
+    int lb, n, chunk, cur, nxt;
+    __device__ __forceinline__ int load(int c, int lane) const {
+        const int j = 64 * c + lane;
+        return j < n ? ent[lb + j] : 0;
+    }
+    __device__ __forceinline__ void init(const int* e, int lb_, int n_, int lane) {
+        ent = e;
+        lb = lb_;
+        n = n_;
+        chunk = 0;
+        cur = load(0, lane);
+        nxt = load(1, lane);
+    }
+    __device__ __forceinline__ int get(int j, int lane) {
+        if ((j >> 6) != chunk) {
+            cur = nxt;
+            ++chunk;
+            nxt = load(chunk + 1, lane);
+        }
+        return __builtin_amdgcn_readlane(cur, j & 63);
+    }
+};
 
-// Staged Q / dO rows: 128 fp16 (256 bytes) per row, the 16-byte chunk c of row q stored at
-// chunk slot c ^ 4*(q % 4) ^ (q / 4 % 4). Sixteen consecutive rows of one chunk (row
-// reads) and a 4-row x 4-chunk block (transposed reads) both land on distinct banks.
-__device__ __forceinline__ int swz(int q, int c) { return c ^ (4 * (q & 3)) ^ ((q >> 2) & 3); }
-__device__ __forceinline__ int swz_off(int q, int col) { return q * HEAD_DIM + swz(q, col >> 3) * 8 + (col & 7); }
-
-// A operand (32 rows x 16 k) whose row m = lane % 32 is column c0 + m of a swizzled
-// [rows][128] fp16 matrix M, k-slots e = 0..3 of the lane being rows r_lo + e and e = 4..7
-// rows r_hi + e - 4.
-__device__ __forceinline__ f16x8 tr_operand_swz(const _Float16* M, int r_lo, int r_hi, int c0, int lane) {
-    const int s = lane & 15;
-    const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (s & 3);
-    const u32x2 lo = ds_read_tr16(M + swz_off(r_lo + (s >> 2), col));
-    const u32x2 hi = ds_read_tr16(M + swz_off(r_hi + (s >> 2), col));
-    return as_f16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-}
-
-// Same for a plain [rows][ld] fp16 matrix.
-__device__ __forceinline__ f16x8 tr_operand(const _Float16* M, int ld, int r_lo, int r_hi, int c0, int lane) {
-    const int s = lane & 15;
-    const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (s & 3);
-    const u32x2 lo = ds_read_tr16(M + (r_lo + (s >> 2)) * ld + col);
-    const u32x2 hi = ds_read_tr16(M + (r_hi + (s >> 2)) * ld + col);
-    return as_f16x8(u32x4{lo[0], lo[1], hi[0], hi[1]});
-}
-
-// 8 bf16 (one 16-byte chunk) -> 8 fp16 scaled by s.
-__device__ __forceinline__ u32x4 bf16x8_to_f16x8_scaled(u32x4 x, float s) {
-    u32x4 r;
+// N MFMAs whose LDS operand (16 bytes per lane) is read three MFMAs ahead of its use. The
+// scheduling fences keep that order; left alone, the compiler tends to wait for each read
+// right before its MFMA.
+template <int N, class Read, class Mma>
+__device__ __forceinline__ void mfma_pipelined(Read read, Mma mma) {
+    u32x4 ring[4];
+    ring[0] = read(0);
+    ring[1] = read(1);
+    ring[2] = read(2);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) r[m] = pack_f16(bf16_lo(x[m]) * s, bf16_hi(x[m]) * s);
-    return r;
+    for (int i = 0; i < N; ++i) {
+        if (i + 3 < N) ring[(i + 3) & 3] = read(i + 3);
+        mma(i, ring[i & 3]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
 }
 
 // Work item: NWK blocks of 32 keys of one KV head, 2 * NWK waves. Waves 0..NWK-1 ("A")
-// compute S -> P and own dV^T and the dQ products; waves NWK..2*NWK-1 ("B") compute dP,
-// receive P through LDS, form dS and own dK^T. Wave w and w + NWK handle the same 32
-// keys and share a SIMD. All products run on fp16 operands: Q, K, V, dO are multiplied
-// by the powers of two sQ, sK, sV, sO while being staged.
+// compute S -> P and own dV^T; waves NWK..2*NWK-1 ("B") compute dP, receive P through LDS,
+// form dS and own dK^T. Wave w and w + NWK handle the same 32 keys and share a SIMD. All
+// products run on fp16 operands: Q, K, V, dO are multiplied by the powers of two sQ, sK,
+// sV, sO while being staged.
+//
+// Each step handles 32 query rows in two halves separated by a barrier:
+//   1: A: S = Q K^T, P -> LDS and registers        B: dP = dO V^T
+//   2: A: dV^T += dO^T P                           B: dS = P * (dP - D), dK^T += Q^T dS
+//      then each role stages its tensor of the next step (A: Q and LSE, B: dO and D) into
+//      the other LDS buffer and issues the global loads of the step after that.
+// The staged rows are double-buffered: buffer s % 2 is read during step s only, and
+// buffer (s + 1) % 2 is written in the second half of step s, after every reader of
+// step s - 1 has passed the barrier that ended it. The two roles run separate loops with
+// the same two barriers per step.
 template <int NWK, bool SPARSE>
 __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
-    constexpr int NT = NWK * 128;
+    constexpr int NR = NWK * 64;          // threads per role
     constexpr int KEYS = NWK * 32;
-    constexpr int CPT = 512 / (NT / 2);     // 16-byte chunks per B thread per tensor per row block
+    constexpr int CPT = 512 / NR;         // 16-byte chunks per thread per staged row block
 
-    __shared__ __attribute__((aligned(16))) _Float16 Qh[32 * HEAD_DIM];    // swizzled rows
-    __shared__ __attribute__((aligned(16))) _Float16 dOh[32 * HEAD_DIM];   // swizzled rows
-    __shared__ __attribute__((aligned(16))) _Float16 Ps[NWK * 2 * 64 * 8];  // [kb][kk][lane][8]
-    __shared__ __attribute__((aligned(16))) float lse_s[32];
-    __shared__ __attribute__((aligned(16))) float dd_s[32];
+    __shared__ __attribute__((aligned(16))) _Float16 Qh[2][32 * HEAD_DIM];    // swizzled rows
+    __shared__ __attribute__((aligned(16))) _Float16 dOh[2][32 * HEAD_DIM];   // swizzled rows
+    __shared__ __attribute__((aligned(16))) _Float16 Ps[NWK * 2 * 64 * 8];    // [kb][kk][lane][8]
+    __shared__ __attribute__((aligned(16))) float lse_s[2][32];
+    __shared__ __attribute__((aligned(16))) float dd_s[2][32];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int l32 = lane & 31, hf = lane >> 5;
     const bool is_a = w < NWK;
     const int kb = is_a ? w : w - NWK;
+    const int rt = is_a ? tid : tid - NR;   // thread index within the role
     const int g = blockIdx.x % a.Hk, y = blockIdx.x / a.Hk;
     const int T = a.T;
 
     // fp16 operand scales (powers of two) from the preprocess bounds
-    const float nrm_do = sqrtf(a.stats[ST_DO_NORM2]), nrm_v = sqrtf(a.stats[ST_V_NORM2]);
-    const float sO = pow2_scale(fmaxf(2.f * nrm_do * nrm_v, nrm_do));
-    const float sQ = pow2_scale(a.stats[ST_Q_ABS]);
-    const float sK = pow2_scale(a.stats[ST_K_ABS]);
-    const float sV = pow2_scale(nrm_v);
+    const OperandScales sc = operand_scales(a.stats);
+    const float sO = sc.sO, sQ = sc.sQ, sK = sc.sK, sV = sc.sV;
     const float cS = a.c / (sQ * sK);       // exponent scale for the scaled scores
     const float inv_sV = 1.f / sV;
 
@@ -277,56 +334,101 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
     const int my_key = key_base + kb * 32 + l32;
     const bool key_ok = my_key < T;
     const size_t kv_row = (size_t)a.Hk * HEAD_DIM;
-    const bf16* kg = a.k + (size_t)g * HEAD_DIM;
-    const bf16* vg = a.v + (size_t)g * HEAD_DIM;
 
-    // A: K rows (B operand of S) and K^T fragments (B operand of dQ); B: V rows (B operand
-    // of dP). All fp16, scaled.
-    const int RB = SPARSE ? a.sblock / 32 : ROWS_PER_WG / 32;   // 32-row blocks per list entry
+    const int lgRB = SPARSE ? (a.sblock == 128 ? 2 : 1) : 3;   // 32-row blocks per list entry
+    const int RB = 1 << lgRB;
     const int nsteps = (le - lb) * RB;
 
-    // Both roles run the same number of steps with three barriers each:
-    //   b1: Q, dO, LSE, D of the row block staged (by B)
-    //   b2: P in LDS (A), dP in registers (B)
-    //   b3: every reader of the staged rows is done
-    // A: [b1] S, P -> LDS [b2] dV [b3]        B: stage [b1] prefetch, dP [b2] dS, dK [b3]
+    // K rows (A: B operand of S) or V rows (B: B operand of dP), fp16 scaled
+    f16x8 kvf[8];
+    {
+        const _Float16* rowp = (is_a ? a.kh : a.vh) + (size_t)g * HEAD_DIM + (size_t)min(my_key, T - 1) * kv_row + 8 * hf;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            u32x4 x = *reinterpret_cast<const u32x4*>(rowp + 16 * ks);
+            if (!key_ok) x = u32x4{0u, 0u, 0u, 0u};
+            kvf[ks] = as_f16x8(x);
+        }
+    }
+
+    EntryStream es;
+    es.init(a.ent, lb, le - lb, lane);
+    int e_cur = 0, e_nxt = 0;   // list entries of this step and the next
+
+    // Staging of this role's tensor (A: Q and LSE, B: dO and D). Rows past the end are
+    // read from a valid row and get LSE = +inf (P = 0) and D = 0 when stored.
+    const _Float16* src = is_a ? a.qh : a.doh;
+    const float* ssrc = is_a ? a.lse : a.dbuf;
+    u32x4 pre[CPT];
+    float praw = 0.f;
+    bool pvalid = false;
+    auto load_rows = [&](int st) {
+        const int e = es.get(st >> lgRB, lane), rb = st & (RB - 1);
+        e_cur = e_nxt;
+        e_nxt = e;
+        const RowMap m = row_map<SPARSE>(a, g, e);
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = rt + i * NR, R = rb * 32 + (c >> 4);
+            const int p = min(m.pos(R), T - 1);
+            pre[i] = *reinterpret_cast<const u32x4*>(src + ((size_t)p * a.Hq + m.head(R)) * HEAD_DIM + (c & 15) * 8);
+        }
+        if (rt < 32) {
+            const int R = rb * 32 + rt, p = m.pos(R);
+            pvalid = p < T;
+            praw = ssrc[(size_t)m.head(R) * T + min(p, T - 1)];
+        }
+    };
+    auto store_rows = [&](int buf) {
+        _Float16* dst = is_a ? Qh[buf] : dOh[buf];
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = rt + i * NR;
+            *reinterpret_cast<u32x4*>(&dst[swz_off(c >> 4, (c & 15) * 8)]) = pre[i];
+        }
+        if (rt < 32) {
+            if (is_a)
+                lse_s[buf][rt] = (!pvalid || praw == -INFINITY) ? INFINITY : praw * LOG2E;
+            else
+                dd_s[buf][rt] = pvalid ? praw * sO : 0.f;
+        }
+    };
+
     f32x16 acc[4];   // A: dV^T, B: dK^T (dims db*32 + acc_row(r, hf), key = lane column)
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
+    if (nsteps > 0) {
+        load_rows(0);
+        store_rows(0);
+        if (nsteps > 1) load_rows(1);
+    }
+    lds_barrier();
+
+    // P and dS slots (hf, e) of 16-row step kk are rows 16*kk + 8*(e/4) + 4*hf + e%4.
     if (is_a) {
-        // K rows (B operand of S)
-        f16x8 kf[8];
-        {
-            const bf16* rowp = kg + (size_t)my_key * kv_row + 8 * hf;
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-                u32x4 x = {0u, 0u, 0u, 0u};
-                if (key_ok) x = *reinterpret_cast<const u32x4*>(rowp + 16 * ks);
-                kf[ks] = as_f16x8(bf16x8_to_f16x8_scaled(x, sK));
-            }
-        }
         int4 kd = {0, 0, 0, 0};
         if (!SPARSE && key_ok) kd = a.desc[my_key];
-
+        // settle the one-time loads here, so no step waits for them behind its prefetches
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         for (int step = 0; step < nsteps; ++step) {
-            const int e = a.ent[lb + step / RB];
-            const int rb = step % RB;
-            const bool full = SPARSE ? true : ((e & 1) != 0);
-            const RowMap rm = row_map<SPARSE>(a, g, e);
-            lds_barrier();   // b1
-
+            const int cb = step & 1;
             // S = Q K^T (scaled by sQ * sK); rows q = acc_row(r, hf)
             f32x16 sacc;
 #pragma unroll
             for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks)
-                sacc = mfma32h(*reinterpret_cast<const f16x8*>(&Qh[swz_off(l32, 16 * ks + 8 * hf)]), kf[ks], sacc);
+            const _Float16* qh = Qh[cb];
+            mfma_pipelined<8>(
+                [&](int ks) { return *reinterpret_cast<const u32x4*>(&qh[swz_off(l32, 16 * ks + 8 * hf)]); },
+                [&](int ks, u32x4 op) { sacc = mfma32h(as_f16x8(op), kvf[ks], sacc); });
+            const int e = e_cur;
+            const bool full = SPARSE ? true : ((e & 1) != 0);
             uint32_t vis = key_ok ? 0xffffu : 0u;
             if (!full && key_ok) {
+                const RowMap rm = row_map<SPARSE>(a, g, e);
+                const int rb = step & (RB - 1);
                 vis = 0u;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
@@ -335,12 +437,11 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
                     vis |= (uint32_t)v << r;
                 }
             }
-            // P (fp16); P and dS slots (hf, e) of step kk are rows 16*kk + 8*(e/4) + 4*hf + e%4
             f16x8 pb[2];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                const float4 l0 = *reinterpret_cast<const float4*>(&lse_s[16 * kk + 4 * hf]);
-                const float4 l1 = *reinterpret_cast<const float4*>(&lse_s[16 * kk + 8 + 4 * hf]);
+                const float4 l0 = *reinterpret_cast<const float4*>(&lse_s[cb][16 * kk + 4 * hf]);
+                const float4 l1 = *reinterpret_cast<const float4*>(&lse_s[cb][16 * kk + 8 + 4 * hf]);
                 const float lr[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
                 u32x4 pk;
 #pragma unroll
@@ -353,93 +454,37 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
                 pb[kk] = as_f16x8(pk);
                 *reinterpret_cast<u32x4*>(&Ps[((kb * 2 + kk) * 64 + lane) * 8]) = pk;
             }
-            lds_barrier();   // b2
+            lds_barrier();   // P of this step in LDS
 
             // dV^T += (dO * sO)^T P
-#pragma unroll
-            for (int db = 0; db < 4; ++db)
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk)
-                    acc[db] = mfma32h(tr_operand_swz(dOh, 16 * kk + 4 * hf, 16 * kk + 8 + 4 * hf, db * 32, lane),
-                                      pb[kk], acc[db]);
-            lds_barrier();   // b3
+            const _Float16* doh = dOh[cb];
+            mfma_pipelined<8>(
+                [&](int i) { return tr_rows_swz(doh, 16 * (i & 1) + 4 * hf, 16 * (i & 1) + 8 + 4 * hf, (i >> 1) * 32, lane); },
+                [&](int i, u32x4 op) { acc[i >> 1] = mfma32h(as_f16x8(op), pb[i & 1], acc[i >> 1]); });
+            if (step + 1 < nsteps) store_rows(cb ^ 1);
+            if (step + 2 < nsteps) load_rows(step + 2);
+            lds_barrier();   // end of step
         }
     } else {
-        // V rows (B operand of dP)
-        f16x8 vf[8];
-        {
-            const bf16* rowp = vg + (size_t)my_key * kv_row + 8 * hf;
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-                u32x4 x = {0u, 0u, 0u, 0u};
-                if (key_ok) x = *reinterpret_cast<const u32x4*>(rowp + 16 * ks);
-                vf[ks] = as_f16x8(bf16x8_to_f16x8_scaled(x, sV));
-            }
-        }
-        const int btid = tid - NWK * 64;
-        u32x4 pq[CPT], pdo[CPT];
-        float pl = INFINITY, pd = 0.f;
-
-#define BWD_LOAD_STEP(st)                                                                      \
-    {                                                                                          \
-        const int e_ = a.ent[lb + (st) / RB], rb_ = (st) % RB;                                 \
-        const RowMap m_ = row_map<SPARSE>(a, g, e_);                                           \
-        _Pragma("unroll") for (int i = 0; i < CPT; ++i) {                                      \
-            const int c_ = btid + i * (NT / 2), R_ = rb_ * 32 + (c_ >> 4), d0_ = (c_ & 15) * 8; \
-            const int p_ = m_.pos(R_);                                                         \
-            const size_t o_ = ((size_t)p_ * a.Hq + m_.head(R_)) * HEAD_DIM + d0_;              \
-            u32x4 z_ = {0u, 0u, 0u, 0u};                                                       \
-            pq[i] = z_;                                                                        \
-            pdo[i] = z_;                                                                       \
-            if (p_ < T) {                                                                      \
-                pq[i] = *reinterpret_cast<const u32x4*>(a.q + o_);                             \
-                pdo[i] = *reinterpret_cast<const u32x4*>(a.dout + o_);                         \
-            }                                                                                  \
-        }                                                                                      \
-        if (btid < 32) {                                                                       \
-            const int p_ = m_.pos(rb_ * 32 + btid), h_ = m_.head(rb_ * 32 + btid);             \
-            pl = INFINITY; /* rows past the end and fully masked rows: P = 0 */                \
-            pd = 0.f;                                                                          \
-            if (p_ < T) {                                                                      \
-                const float lse_ = a.lse[(size_t)h_ * T + p_];                                 \
-                pl = lse_ == -INFINITY ? INFINITY : lse_ * LOG2E;                              \
-                pd = a.dbuf[(size_t)h_ * T + p_] * sO;                                         \
-            }                                                                                  \
-        }                                                                                      \
-    }
-
-        if (nsteps > 0) BWD_LOAD_STEP(0);
         for (int step = 0; step < nsteps; ++step) {
-            // stage Q * sQ and dO * sO as swizzled fp16 rows, LSE (base 2) and D * sO
-#pragma unroll
-            for (int i = 0; i < CPT; ++i) {
-                const int c = btid + i * (NT / 2), q = c >> 4, d0 = (c & 15) * 8;
-                *reinterpret_cast<u32x4*>(&Qh[swz_off(q, d0)]) = bf16x8_to_f16x8_scaled(pq[i], sQ);
-                *reinterpret_cast<u32x4*>(&dOh[swz_off(q, d0)]) = bf16x8_to_f16x8_scaled(pdo[i], sO);
-            }
-            if (btid < 32) {
-                lse_s[btid] = pl;
-                dd_s[btid] = pd;
-            }
-            lds_barrier();   // b1
-            if (step + 1 < nsteps) BWD_LOAD_STEP(step + 1);
-
+            const int cb = step & 1;
             // dP = dO V^T (scaled by sO * sV)
             f32x16 dpacc;
 #pragma unroll
             for (int r = 0; r < 16; ++r) dpacc[r] = 0.f;
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks)
-                dpacc = mfma32h(*reinterpret_cast<const f16x8*>(&dOh[swz_off(l32, 16 * ks + 8 * hf)]), vf[ks], dpacc);
-            lds_barrier();   // b2
+            const _Float16* doh = dOh[cb];
+            mfma_pipelined<8>(
+                [&](int ks) { return *reinterpret_cast<const u32x4*>(&doh[swz_off(l32, 16 * ks + 8 * hf)]); },
+                [&](int ks, u32x4 op) { dpacc = mfma32h(as_f16x8(op), kvf[ks], dpacc); });
+            lds_barrier();   // P of this step in LDS
 
             // dS * sO = P * (dP * sO - D * sO); dK^T += (Q * sQ)^T (dS * sO)
             f16x8 sb[2];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 const f16x8 ph = as_f16x8(*reinterpret_cast<const u32x4*>(&Ps[((kb * 2 + kk) * 64 + lane) * 8]));
-                const float4 d0v = *reinterpret_cast<const float4*>(&dd_s[16 * kk + 4 * hf]);
-                const float4 d1v = *reinterpret_cast<const float4*>(&dd_s[16 * kk + 8 + 4 * hf]);
+                const float4 d0v = *reinterpret_cast<const float4*>(&dd_s[cb][16 * kk + 4 * hf]);
+                const float4 d1v = *reinterpret_cast<const float4*>(&dd_s[cb][16 * kk + 8 + 4 * hf]);
                 const float dr[8] = {d0v.x, d0v.y, d0v.z, d0v.w, d1v.x, d1v.y, d1v.z, d1v.w};
                 u32x4 sk;
 #pragma unroll
@@ -451,15 +496,14 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
                 }
                 sb[kk] = as_f16x8(sk);
             }
-#pragma unroll
-            for (int db = 0; db < 4; ++db)
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk)
-                    acc[db] = mfma32h(tr_operand_swz(Qh, 16 * kk + 4 * hf, 16 * kk + 8 + 4 * hf, db * 32, lane),
-                                      sb[kk], acc[db]);
-            lds_barrier();   // b3
+            const _Float16* qh = Qh[cb];
+            mfma_pipelined<8>(
+                [&](int i) { return tr_rows_swz(qh, 16 * (i & 1) + 4 * hf, 16 * (i & 1) + 8 + 4 * hf, (i >> 1) * 32, lane); },
+                [&](int i, u32x4 op) { acc[i >> 1] = mfma32h(as_f16x8(op), sb[i & 1], acc[i >> 1]); });
+            if (step + 1 < nsteps) store_rows(cb ^ 1);
+            if (step + 2 < nsteps) load_rows(step + 2);
+            lds_barrier();   // end of step
         }
-#undef BWD_LOAD_STEP
     }
 
     if (key_ok) {
@@ -502,11 +546,8 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
     const int g = blockIdx.x % a.Hk, y = blockIdx.x / a.Hk;
     const int T = a.T;
 
-    const float nrm_do = sqrtf(a.stats[ST_DO_NORM2]), nrm_v = sqrtf(a.stats[ST_V_NORM2]);
-    const float sO = pow2_scale(fmaxf(2.f * nrm_do * nrm_v, nrm_do));
-    const float sQ = pow2_scale(a.stats[ST_Q_ABS]);
-    const float sK = pow2_scale(a.stats[ST_K_ABS]);
-    const float sV = pow2_scale(nrm_v);
+    const OperandScales sc = operand_scales(a.stats);
+    const float sO = sc.sO, sQ = sc.sQ, sK = sc.sK, sV = sc.sV;
     const float cS = a.c / (sQ * sK);
     const float inv_sV = 1.f / sV;
 
@@ -538,11 +579,11 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
         for (int ks = 0; ks < 8; ++ks) {
             u32x4 x = {0u, 0u, 0u, 0u}, z = {0u, 0u, 0u, 0u};
             if (row_ok) {
-                x = *reinterpret_cast<const u32x4*>(a.q + ro + 16 * ks);
-                z = *reinterpret_cast<const u32x4*>(a.dout + ro + 16 * ks);
+                x = *reinterpret_cast<const u32x4*>(a.qh + ro + 16 * ks);
+                z = *reinterpret_cast<const u32x4*>(a.doh + ro + 16 * ks);
             }
-            qf[ks] = as_f16x8(bf16x8_to_f16x8_scaled(x, sQ));
-            df[ks] = as_f16x8(bf16x8_to_f16x8_scaled(z, sO));
+            qf[ks] = as_f16x8(x);
+            df[ks] = as_f16x8(z);
         }
         if (row_ok) {
             const float l = a.lse[(size_t)head * T + pos];
@@ -557,8 +598,8 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
-    const bf16* kbase = a.k + (size_t)g * HEAD_DIM;
-    const bf16* vbase = a.v + (size_t)g * HEAD_DIM;
+    const _Float16* kbase = a.kh + (size_t)g * HEAD_DIM;
+    const _Float16* vbase = a.vh + (size_t)g * HEAD_DIM;
     const size_t kv_row = (size_t)a.Hk * HEAD_DIM;
     u32x4 kreg[CPT], vreg[CPT];
     int4 dreg = {0, 0, 0, 0};
@@ -604,8 +645,8 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const int c = tid + i * NT, row = c >> 4, d0 = (c & 15) * 8;
-            *reinterpret_cast<u32x4*>(&Kh[swz_off(row, d0)]) = bf16x8_to_f16x8_scaled(kreg[i], sK);
-            *reinterpret_cast<u32x4*>(&Vh[swz_off(row, d0)]) = bf16x8_to_f16x8_scaled(vreg[i], sV);
+            *reinterpret_cast<u32x4*>(&Kh[swz_off(row, d0)]) = kreg[i];
+            *reinterpret_cast<u32x4*>(&Vh[swz_off(row, d0)]) = vreg[i];
         }
         if (!SPARSE && need_mask && tid < FWD_BN) Ds[tid] = dreg;
         lds_barrier();
@@ -685,7 +726,9 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
 
 hipError_t launch_bwd_pre(const Problem& P, const void* q, const void* k, const void* v, const void* o,
                           const void* o_lo, const void* dout, float* dbuf, hipStream_t s) {
-    float* stats = reinterpret_cast<float*>(reinterpret_cast<char*>(dbuf) + bwd_stats_offset(P.Hq, P.T));
+    const BwdLayout W = bwd_layout(P.Hq, P.Hk, P.T);
+    char* ws = reinterpret_cast<char*>(dbuf);
+    float* stats = reinterpret_cast<float*>(ws + W.stats);
     hipLaunchKernelGGL(zero_stats_kernel, dim3(1), dim3(64), 0, s, stats);
     const long rows = (long)P.T * P.Hq;
     hipLaunchKernelGGL(bwd_pre_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s,
@@ -698,6 +741,10 @@ hipError_t launch_bwd_pre(const Problem& P, const void* q, const void* k, const 
                        stats + ST_K_ABS);
     hipLaunchKernelGGL(rownorm_kernel, dim3(256), dim3(256), 0, s, static_cast<const bf16*>(v),
                        (long)P.T * P.Hk, stats + ST_V_NORM2);
+    hipLaunchKernelGGL(to_f16_kernel, dim3(2048), dim3(256), 0, s, static_cast<const u32x4*>(q),
+                       static_cast<const u32x4*>(dout), static_cast<const u32x4*>(k), static_cast<const u32x4*>(v),
+                       reinterpret_cast<u32x4*>(ws + W.qh), reinterpret_cast<u32x4*>(ws + W.doh),
+                       reinterpret_cast<u32x4*>(ws + W.kh), reinterpret_cast<u32x4*>(ws + W.vh), nq8, nk8, stats);
     return hipGetLastError();
 }
 
@@ -713,7 +760,13 @@ hipError_t launch_bwd_main(const Problem& P, const void* q, const void* k, const
     a.dout = static_cast<const bf16*>(dout);
     a.lse = lse;
     a.dbuf = dbuf;
-    a.stats = reinterpret_cast<const float*>(reinterpret_cast<const char*>(dbuf) + bwd_stats_offset(P.Hq, P.T));
+    const BwdLayout W = bwd_layout(P.Hq, P.Hk, P.T);
+    const char* ws = reinterpret_cast<const char*>(dbuf);
+    a.stats = reinterpret_cast<const float*>(ws + W.stats);
+    a.qh = reinterpret_cast<const _Float16*>(ws + W.qh);
+    a.doh = reinterpret_cast<const _Float16*>(ws + W.doh);
+    a.kh = reinterpret_cast<const _Float16*>(ws + W.kh);
+    a.vh = reinterpret_cast<const _Float16*>(ws + W.vh);
     a.dq = dq;
     a.dk = dk;
     a.dv = dv;

@@ -81,6 +81,37 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Transposed LDS read (ds_read_b64_tr_b16): within each group of 16 lanes, source lane s
+// supplies the address of 4 consecutive 16-bit elements and output lane i receives
+// element i % 4 of source lanes i/4, i/4 + 4, i/4 + 8, i/4 + 12. With source lane s
+// pointing at M[r0 + s/4][c0 + 4*(s%4)], output lane i gets M[r0 .. r0+3][c0 + i].
+__device__ __forceinline__ u32x2 ds_read_tr16(const void* p) {
+    typedef short i16x4 __attribute__((ext_vector_type(4)));
+    const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+    return __builtin_bit_cast(u32x2, v);
+}
+
+// Staged Q / dO rows: 128 fp16 (256 bytes) per row, the 16-byte chunk c of row q stored at
+// chunk slot c ^ 4*(q % 4) ^ (q / 4 % 4). Sixteen consecutive rows of one chunk (row
+// reads) and a 4-row x 4-chunk block (transposed reads) both land on distinct banks.
+__device__ __forceinline__ int swz(int q, int c) { return c ^ (4 * (q & 3)) ^ ((q >> 2) & 3); }
+__device__ __forceinline__ int swz_off(int q, int col) { return q * HEAD_DIM + swz(q, col >> 3) * 8 + (col & 7); }
+
+// A operand (32 rows x 16 k) of 16-bit elements whose row m = lane % 32 is column c0 + m
+// of a swizzled [rows][128] matrix M, k-slots e = 0..3 of the lane being rows r_lo + e and
+// e = 4..7 rows r_hi + e - 4 (callers fold the lane half into r_lo / r_hi).
+__device__ __forceinline__ u32x4 tr_rows_swz(const void* M, int r_lo, int r_hi, int c0, int lane) {
+    const uint16_t* m = static_cast<const uint16_t*>(M);
+    const int s = lane & 15;
+    const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (s & 3);
+    const u32x2 lo = ds_read_tr16(m + swz_off(r_lo + (s >> 2), col));
+    const u32x2 hi = ds_read_tr16(m + swz_off(r_hi + (s >> 2), col));
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+__device__ __forceinline__ f16x8 tr_operand_swz(const _Float16* M, int r_lo, int r_hi, int c0, int lane) {
+    return as_f16x8(tr_rows_swz(M, r_lo, r_hi, c0, lane));
+}
+
 // Round an offset up to 256 bytes.
 __host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -99,11 +130,24 @@ struct Problem {
     int nb;
 };
 
-// Backward workspace: D [Hq][T] fp32, then BWD_STATS fp32 bounds used to pick the
-// power-of-two scales of the fp16 operands (see bwd.hip).
+// Backward workspace, in order (each part 256-byte aligned):
+//   D [Hq][T] fp32 | BWD_STATS fp32 bounds of the operands | Q, dO [T][Hq][128] and
+//   K, V [T][Hk][128] as fp16 multiplied by their power-of-two scales (see bwd.hip).
 constexpr int BWD_STATS = 4;
-__host__ __device__ constexpr size_t bwd_stats_offset(int Hq, int T) { return align256((size_t)Hq * T * 4); }
-__host__ __device__ constexpr size_t bwd_workspace_bytes(int Hq, int T) { return bwd_stats_offset(Hq, T) + 256; }
+struct BwdLayout {
+    size_t stats, qh, doh, kh, vh, total;
+};
+__host__ __device__ inline BwdLayout bwd_layout(int Hq, int Hk, int T) {
+    BwdLayout L;
+    const size_t qbytes = align256((size_t)T * Hq * 128 * 2), kbytes = align256((size_t)T * Hk * 128 * 2);
+    L.stats = align256((size_t)Hq * T * 4);
+    L.qh = L.stats + 256;
+    L.doh = L.qh + qbytes;
+    L.kh = L.doh + qbytes;
+    L.vh = L.kh + kbytes;
+    L.total = L.vh + kbytes;
+    return L;
+}
 
 struct IndexLayout {
     size_t fwd_cls, fwd_ptr, fwd_ent, fwd_order;
