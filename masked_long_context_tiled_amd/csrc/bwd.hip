@@ -529,17 +529,21 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
 // row: S^T = K Q^T and dP^T = V dO^T (A = K / V rows from LDS, B = the wave's Q / dO rows
 // in registers), then P^T, dS^T = P^T * (dP^T - D) with the row's LSE and D as per-lane
 // scalars, and dQ^T += K^T dS^T with K^T read from the same LDS tile by transposed reads
-// and dS^T straight from the accumulators as the B operand. Operands are fp16 scaled by
-// the same powers of two as the main backward kernel.
+// and dS^T straight from the accumulators as the B operand. Operands are the preprocess's
+// fp16 copies, scaled by the same powers of two as in the dK/dV kernel.
+//
+// K, V and the column descriptors are double-buffered in LDS: while tile t is computed
+// from slot t % 2, tile t + 1 (loaded one tile earlier) is stored into the other slot and
+// the loads of tile t + 2 are issued; one barrier per tile.
 template <int NW, bool SPARSE>
 __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
     constexpr int NT = NW * 64;
     constexpr int CPT = 1024 / NT;               // 16-byte chunks per thread per tile per tensor
     constexpr int TPE = SPARSE ? NW / 2 : 1;     // 64-key tiles per list entry
 
-    __shared__ __attribute__((aligned(16))) _Float16 Kh[FWD_BN * HEAD_DIM];   // swizzled rows
-    __shared__ __attribute__((aligned(16))) _Float16 Vh[FWD_BN * HEAD_DIM];   // swizzled rows
-    __shared__ int4 Ds[FWD_BN];
+    __shared__ __attribute__((aligned(16))) _Float16 Kh[2][FWD_BN * HEAD_DIM];   // swizzled rows
+    __shared__ __attribute__((aligned(16))) _Float16 Vh[2][FWD_BN * HEAD_DIM];   // swizzled rows
+    __shared__ int4 Ds[2][FWD_BN];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int l32 = lane & 31, hf = lane >> 5;
@@ -574,22 +578,17 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
     float lse2 = INFINITY, dd = 0.f;
     f16x8 qf[8], df[8];
     {
-        const size_t ro = ((size_t)pos * a.Hq + head) * HEAD_DIM + 8 * hf;
+        const size_t ro = ((size_t)min(pos, T - 1) * a.Hq + head) * HEAD_DIM + 8 * hf;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
-            u32x4 x = {0u, 0u, 0u, 0u}, z = {0u, 0u, 0u, 0u};
-            if (row_ok) {
-                x = *reinterpret_cast<const u32x4*>(a.qh + ro + 16 * ks);
-                z = *reinterpret_cast<const u32x4*>(a.doh + ro + 16 * ks);
-            }
-            qf[ks] = as_f16x8(x);
-            df[ks] = as_f16x8(z);
+            qf[ks] = as_f16x8(*reinterpret_cast<const u32x4*>(a.qh + ro + 16 * ks));
+            df[ks] = as_f16x8(*reinterpret_cast<const u32x4*>(a.doh + ro + 16 * ks));
         }
-        if (row_ok) {
-            const float l = a.lse[(size_t)head * T + pos];
-            lse2 = l == -INFINITY ? INFINITY : l * LOG2E;
-            dd = a.dbuf[(size_t)head * T + pos] * sO;
-        }
+        const float l = a.lse[(size_t)head * T + min(pos, T - 1)];
+        const float d = a.dbuf[(size_t)head * T + min(pos, T - 1)];
+        // rows past the end: P = 0
+        lse2 = (!row_ok || l == -INFINITY) ? INFINITY : l * LOG2E;
+        dd = row_ok ? d * sO : 0.f;
     }
 
     f32x16 acc[4];   // dQ^T: dims db*32 + acc_row(r, hf), query = lane column
@@ -601,58 +600,68 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
     const _Float16* kbase = a.kh + (size_t)g * HEAD_DIM;
     const _Float16* vbase = a.vh + (size_t)g * HEAD_DIM;
     const size_t kv_row = (size_t)a.Hk * HEAD_DIM;
+
+    EntryStream es;
+    es.init(a.ent, lb, le - lb, lane);
+    // first key and "needs per-element masking" of tiles t (cur) and t + 1 (nxt)
+    int key0_cur = 0, key0_nxt = 0;
+    bool mask_cur = false, mask_nxt = false;
+
+    // Rows past the end are read from row T - 1 (finite data; such keys are masked).
     u32x4 kreg[CPT], vreg[CPT];
     int4 dreg = {0, 0, 0, 0};
-    int nkey0 = 0;
-    bool nmask = false;
-
-#define DQ_LOAD_TILE(t)                                                                        \
-    {                                                                                          \
-        const int e_ = a.ent[lb + (t) / TPE];                                                  \
-        bool full_;                                                                            \
-        if constexpr (SPARSE) {                                                                \
-            nkey0 = e_ * a.sblock + ((t) % TPE) * FWD_BN;                                      \
-            full_ = true;                                                                      \
-        } else {                                                                               \
-            nkey0 = (e_ >> 1) * FWD_BN;                                                        \
-            full_ = (e_ & 1) != 0;                                                             \
-        }                                                                                      \
-        nmask = !full_ || nkey0 + FWD_BN > T;                                                  \
-        _Pragma("unroll") for (int i = 0; i < CPT; ++i) {                                      \
-            const int c_ = tid + i * NT, key_ = nkey0 + (c_ >> 4);                             \
-            const size_t o_ = (size_t)key_ * kv_row + (c_ & 15) * 8;                           \
-            u32x4 x_ = {0u, 0u, 0u, 0u}, z_ = {0u, 0u, 0u, 0u};                                \
-            if (key_ < T) {                                                                    \
-                x_ = *reinterpret_cast<const u32x4*>(kbase + o_);                              \
-                z_ = *reinterpret_cast<const u32x4*>(vbase + o_);                              \
-            }                                                                                  \
-            kreg[i] = x_;                                                                      \
-            vreg[i] = z_;                                                                      \
-        }                                                                                      \
-        if (!SPARSE && nmask && tid < FWD_BN) {                                                \
-            const int key_ = nkey0 + tid;                                                      \
-            dreg = key_ < T ? a.desc[key_] : int4{0, 0, 0, 0};                                 \
-        }                                                                                      \
-    }
-
-    if (ntiles > 0) DQ_LOAD_TILE(0);
-
-    for (int t = 0; t < ntiles; ++t) {
-        const int key0 = nkey0;
-        const bool need_mask = nmask;
-
-        lds_barrier();   // every wave is done reading the previous tile
+    bool dzero = false;
+    auto load_tile = [&](int t) {
+        const int e = es.get(t / TPE, lane);
+        int key0;
+        bool full;
+        if constexpr (SPARSE) {
+            key0 = e * a.sblock + (t % TPE) * FWD_BN;
+            full = true;
+        } else {
+            key0 = (e >> 1) * FWD_BN;
+            full = (e & 1) != 0;
+        }
+        key0_cur = key0_nxt;
+        mask_cur = mask_nxt;
+        key0_nxt = key0;
+        mask_nxt = !full || key0 + FWD_BN > T;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = tid + i * NT, key = min(key0 + (c >> 4), T - 1);
+            const size_t o = (size_t)key * kv_row + (c & 15) * 8;
+            kreg[i] = *reinterpret_cast<const u32x4*>(kbase + o);
+            vreg[i] = *reinterpret_cast<const u32x4*>(vbase + o);
+        }
+        if (!SPARSE && tid < FWD_BN) {
+            const int key = key0 + tid;
+            dreg = a.desc[min(key, T - 1)];
+            dzero = key >= T;
+        }
+    };
+    auto store_tile = [&](int slot) {
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const int c = tid + i * NT, row = c >> 4, d0 = (c & 15) * 8;
-            *reinterpret_cast<u32x4*>(&Kh[swz_off(row, d0)]) = kreg[i];
-            *reinterpret_cast<u32x4*>(&Vh[swz_off(row, d0)]) = vreg[i];
+            *reinterpret_cast<u32x4*>(&Kh[slot][swz_off(row, d0)]) = kreg[i];
+            *reinterpret_cast<u32x4*>(&Vh[slot][swz_off(row, d0)]) = vreg[i];
         }
-        if (!SPARSE && need_mask && tid < FWD_BN) Ds[tid] = dreg;
-        lds_barrier();
+        if (!SPARSE && tid < FWD_BN) Ds[slot][tid] = dzero ? int4{0, 0, 0, 0} : dreg;
+    };
 
-        if (t + 1 < ntiles) DQ_LOAD_TILE(t + 1);
+    if (ntiles > 0) {
+        load_tile(0);
+        store_tile(0);
+        if (ntiles > 1) load_tile(1);
+    }
+    lds_barrier();
 
+    for (int t = 0; t < ntiles; ++t) {
+        const int cb = t & 1;
+        const int key0 = t + 1 < ntiles ? key0_cur : key0_nxt;
+        const bool need_mask = t + 1 < ntiles ? mask_cur : mask_nxt;
+        const _Float16* kt = Kh[cb];
+        const _Float16* vt = Vh[cb];
         // per 32-key half kb: S^T = K Q^T and dP^T = V dO^T (lane column = its query row,
         // rows = keys), dS^T, then dQ^T += (K * sK)^T (dS^T * sO) for those 32 keys
 #pragma unroll
@@ -663,12 +672,15 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
                 st[r] = 0.f;
                 dpt[r] = 0.f;
             }
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks) {
-                const int off = swz_off(kb * 32 + l32, 16 * ks + 8 * hf);
-                st = mfma32h(*reinterpret_cast<const f16x8*>(&Kh[off]), qf[ks], st);
-                dpt = mfma32h(*reinterpret_cast<const f16x8*>(&Vh[off]), df[ks], dpt);
-            }
+            mfma_pipelined<16>(
+                [&](int i) {
+                    const int off = swz_off(kb * 32 + l32, 16 * (i >> 1) + 8 * hf);
+                    return *reinterpret_cast<const u32x4*>(((i & 1) ? vt : kt) + off);
+                },
+                [&](int i, u32x4 op) {
+                    if (i & 1) dpt = mfma32h(as_f16x8(op), df[i >> 1], dpt);
+                    else st = mfma32h(as_f16x8(op), qf[i >> 1], st);
+                });
             // dS^T * sO = P^T * (dP^T * sO - D * sO), as B operands of two 16-key steps;
             // key slot (hf, e) of step kk is key kb*32 + 16*kk + 8*(e/4) + 4*hf + e%4
             f16x8 sb[2];
@@ -687,8 +699,9 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
                             if constexpr (SPARSE) {
                                 vis = key0 + kidx < T;
                             } else {
-                                const int4 d = Ds[kidx];
-                                vis = (pos >= d.x && pos < d.y) || (pos >= d.z && pos < d.w);
+                                const int4 d = Ds[cb][kidx];
+                                vis = ((unsigned)(pos - d.x) < (unsigned)(d.y - d.x)) |
+                                      ((unsigned)(pos - d.z) < (unsigned)(d.w - d.z));
                             }
                         }
                         const float p = vis ? fast_exp2(fmaf(st[r], cS, -lse2)) : 0.f;
@@ -698,16 +711,19 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
                 }
                 sb[kk] = as_f16x8(pk);
             }
-#pragma unroll
-            for (int db = 0; db < 4; ++db)
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    const int k0 = kb * 32 + 16 * kk + 4 * hf;
-                    acc[db] = mfma32h(tr_operand_swz(Kh, k0, k0 + 8, db * 32, lane), sb[kk], acc[db]);
-                }
+            mfma_pipelined<8>(
+                [&](int i) {
+                    const int k0 = kb * 32 + 16 * (i & 1) + 4 * hf;
+                    return tr_rows_swz(kt, k0, k0 + 8, (i >> 1) * 32, lane);
+                },
+                [&](int i, u32x4 op) { acc[i >> 1] = mfma32h(as_f16x8(op), sb[i & 1], acc[i >> 1]); });
         }
+        // tile t + 1 into the other slot (its readers of tile t - 1 passed the last
+        // barrier), loads of tile t + 2
+        if (t + 1 < ntiles) store_tile(cb ^ 1);
+        if (t + 2 < ntiles) load_tile(t + 2);
+        lds_barrier();
     }
-#undef DQ_LOAD_TILE
 
     if (row_ok) {
         const float unscale = a.scale / (sO * sK);
