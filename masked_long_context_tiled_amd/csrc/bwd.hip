@@ -362,16 +362,28 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
     u32x4 pre[CPT];
     float praw = 0.f;
     bool pvalid = false;
+    const int span = SPARSE ? a.sblock : a.BMq;   // positions per list entry
     auto load_rows = [&](int st) {
         const int e = es.get(st >> lgRB, lane), rb = st & (RB - 1);
         e_cur = e_nxt;
         e_nxt = e;
         const RowMap m = row_map<SPARSE>(a, g, e);
+        if (m.pbase + span <= T) {
+            // one base per step plus small per-lane offsets
+            const _Float16* base = src + ((size_t)m.pbase * a.Hq + m.hbase) * HEAD_DIM;
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int c = rt + i * NR, R = rb * 32 + (c >> 4);
-            const int p = min(m.pos(R), T - 1);
-            pre[i] = *reinterpret_cast<const u32x4*>(src + ((size_t)p * a.Hq + m.head(R)) * HEAD_DIM + (c & 15) * 8);
+            for (int i = 0; i < CPT; ++i) {
+                const int c = rt + i * NR, R = rb * 32 + (c >> 4);
+                const unsigned off = (unsigned)((((R & m.mask) * a.Hq + (R >> m.lg)) * HEAD_DIM) + (c & 15) * 8);
+                pre[i] = *reinterpret_cast<const u32x4*>(base + off);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) {
+                const int c = rt + i * NR, R = rb * 32 + (c >> 4);
+                const int p = min(m.pos(R), T - 1);
+                pre[i] = *reinterpret_cast<const u32x4*>(src + ((size_t)p * a.Hq + m.head(R)) * HEAD_DIM + (c & 15) * 8);
+            }
         }
         if (rt < 32) {
             const int R = rb * 32 + rt, p = m.pos(R);
@@ -438,18 +450,28 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
                 }
             }
             f16x8 pb[2];
+            const bool all_vis = full && key_base + KEYS <= T;   // no element of the step masked
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 const float4 l0 = *reinterpret_cast<const float4*>(&lse_s[cb][16 * kk + 4 * hf]);
                 const float4 l1 = *reinterpret_cast<const float4*>(&lse_s[cb][16 * kk + 8 + 4 * hf]);
                 const float lr[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
                 u32x4 pk;
+                if (all_vis) {
 #pragma unroll
-                for (int e2 = 0; e2 < 8; e2 += 2) {
-                    const int r0 = kk * 8 + e2, r1 = r0 + 1;
-                    const float p0 = fast_exp2(fmaf(sacc[r0], cS, -lr[e2]));
-                    const float p1 = fast_exp2(fmaf(sacc[r1], cS, -lr[e2 + 1]));
-                    pk[e2 >> 1] = pack_f16(((vis >> r0) & 1u) ? p0 : 0.f, ((vis >> r1) & 1u) ? p1 : 0.f);
+                    for (int e2 = 0; e2 < 8; e2 += 2) {
+                        const int r0 = kk * 8 + e2;
+                        pk[e2 >> 1] = pack_f16(fast_exp2(fmaf(sacc[r0], cS, -lr[e2])),
+                                               fast_exp2(fmaf(sacc[r0 + 1], cS, -lr[e2 + 1])));
+                    }
+                } else {
+#pragma unroll
+                    for (int e2 = 0; e2 < 8; e2 += 2) {
+                        const int r0 = kk * 8 + e2, r1 = r0 + 1;
+                        const float p0 = fast_exp2(fmaf(sacc[r0], cS, -lr[e2]));
+                        const float p1 = fast_exp2(fmaf(sacc[r1], cS, -lr[e2 + 1]));
+                        pk[e2 >> 1] = pack_f16(((vis >> r0) & 1u) ? p0 : 0.f, ((vis >> r1) & 1u) ? p1 : 0.f);
+                    }
                 }
                 pb[kk] = as_f16x8(pk);
                 *reinterpret_cast<u32x4*>(&Ps[((kb * 2 + kk) * 64 + lane) * 8]) = pk;
@@ -486,15 +508,21 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
                 const float4 d0v = *reinterpret_cast<const float4*>(&dd_s[cb][16 * kk + 4 * hf]);
                 const float4 d1v = *reinterpret_cast<const float4*>(&dd_s[cb][16 * kk + 8 + 4 * hf]);
                 const float dr[8] = {d0v.x, d0v.y, d0v.z, d0v.w, d1v.x, d1v.y, d1v.z, d1v.w};
-                u32x4 sk;
+                // (dP - D) in fp32, rounded to fp16, times P in packed fp16
+                f16x8 sk;
 #pragma unroll
                 for (int e2 = 0; e2 < 8; e2 += 2) {
                     const int r0 = kk * 8 + e2, r1 = r0 + 1;
-                    const float x0 = (float)ph[e2] * fmaf(dpacc[r0], inv_sV, -dr[e2]);
-                    const float x1 = (float)ph[e2 + 1] * fmaf(dpacc[r1], inv_sV, -dr[e2 + 1]);
-                    sk[e2 >> 1] = pack_f16(x0, x1);
+                    f16x2 t, pp;
+                    t[0] = (_Float16)fmaf(dpacc[r0], inv_sV, -dr[e2]);
+                    t[1] = (_Float16)fmaf(dpacc[r1], inv_sV, -dr[e2 + 1]);
+                    pp[0] = ph[e2];
+                    pp[1] = ph[e2 + 1];
+                    const f16x2 x = t * pp;
+                    sk[e2] = x[0];
+                    sk[e2 + 1] = x[1];
                 }
-                sb[kk] = as_f16x8(sk);
+                sb[kk] = sk;
             }
             const _Float16* qh = Qh[cb];
             mfma_pipelined<8>(
