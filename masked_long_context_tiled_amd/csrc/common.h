@@ -92,6 +92,52 @@ __device__ __forceinline__ u32x2 ds_read_tr16(const void* p) {
     return __builtin_bit_cast(u32x2, v);
 }
 
+// List entries of a work item, 64 per register: lane i of chunk register c holds entry
+// 64 c + i. Entries are read in non-decreasing order; the chunk after the current one is
+// loaded a whole chunk ahead and only touched (waited for) when the reader moves on to it.
+struct EntryStream {
+    const int* ent;
+    int lb, n, chunk, cur, nxt;
+    __device__ __forceinline__ int load(int c, int lane) const {
+        const int j = 64 * c + lane;
+        return j < n ? ent[lb + j] : 0;
+    }
+    __device__ __forceinline__ void init(const int* e, int lb_, int n_, int lane) {
+        ent = e;
+        lb = lb_;
+        n = n_;
+        chunk = 0;
+        cur = load(0, lane);
+        nxt = load(1, lane);
+    }
+    __device__ __forceinline__ int get(int j, int lane) {
+        if ((j >> 6) != chunk) {
+            cur = nxt;
+            ++chunk;
+            nxt = load(chunk + 1, lane);
+        }
+        return __builtin_amdgcn_readlane(cur, j & 63);
+    }
+};
+
+// N MFMAs whose LDS operand (16 bytes per lane) is read three MFMAs ahead of its use. The
+// scheduling fences keep that order; left alone, the compiler tends to wait for each read
+// right before its MFMA.
+template <int N, class Read, class Mma>
+__device__ __forceinline__ void mfma_pipelined(Read read, Mma mma) {
+    u32x4 ring[4];
+    ring[0] = read(0);
+    ring[1] = read(1);
+    ring[2] = read(2);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        if (i + 3 < N) ring[(i + 3) & 3] = read(i + 3);
+        mma(i, ring[i & 3]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 // Staged Q / dO rows: 128 fp16 (256 bytes) per row, the 16-byte chunk c of row q stored at
 // chunk slot c ^ 4*(q % 4) ^ (q / 4 % 4). Sixteen consecutive rows of one chunk (row
 // reads) and a 4-row x 4-chunk block (transposed reads) both land on distinct banks.

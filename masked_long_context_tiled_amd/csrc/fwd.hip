@@ -38,7 +38,7 @@ struct FwdArgs {
     const int* ptr;
     const int* ent;
     const int* order;
-    int T, Hq, Hk, G, BMq, nb, sblock;
+    int T, Hq, Hk, G, BMq, lgBMq, nb, sblock;
     float c;   // scale * log2(e)
 };
 
@@ -274,6 +274,223 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
     }
 }
 
+// Dense work items (the G heads of one KV head x 256/G positions, 8 waves of 32 rows).
+// Same arithmetic as fwd_kernel, organised for fewer stalls:
+//  - K, V and the column descriptors are double-buffered in LDS: while tile t is
+//    computed from slot t % 2, tile t + 1 (loaded one tile earlier) is stored into the
+//    other slot and the loads of tile t + 2 are issued; one barrier per tile;
+//  - V is kept row-major and V^T is read with transposed LDS reads (no transposing
+//    stores); the row strides (136 and 144 bf16) make both K's row reads and V's
+//    transposed reads free of bank conflicts;
+//  - every MFMA's LDS operand is read three MFMAs ahead;
+//  - list entries are read from registers filled a chunk ahead, so no load waits on a
+//    freshly loaded entry;
+//  - the in-lane row max covers half of a row's keys; the two halves are combined only
+//    when the running max has to move (the lazy rescale).
+constexpr int K_LD = HEAD_DIM + 8;    // bf16 per K row in LDS
+constexpr int V_LD = HEAD_DIM + 16;   // bf16 per V row in LDS
+
+// A operand (32 rows x 16 k) of 16-bit elements whose row m = lane % 32 is column c0 + m
+// of the row-major [rows][ld] matrix M; k-slots e = 0..3 are rows r_lo + e, e = 4..7 rows
+// r_hi + e - 4 (callers fold the lane half into r_lo / r_hi).
+__device__ __forceinline__ u32x4 tr_rows_ld(const bf16* M, int ld, int r_lo, int r_hi, int c0, int lane) {
+    const int s = lane & 15;
+    const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (s & 3);
+    const u32x2 lo = ds_read_tr16(M + (r_lo + (s >> 2)) * ld + col);
+    const u32x2 hi = ds_read_tr16(M + (r_hi + (s >> 2)) * ld + col);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+__global__ __launch_bounds__(512) void fwd_dense_kernel(FwdArgs a) {
+    constexpr int NT = 512;
+    constexpr int CPT = 1024 / NT;   // 16-byte chunks per thread per tile per tensor
+
+    __shared__ __attribute__((aligned(16))) bf16 Kb[2][FWD_BN * K_LD];
+    __shared__ __attribute__((aligned(16))) bf16 Vb[2][FWD_BN * V_LD];
+    __shared__ int4 Db[2][FWD_BN];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int l32 = lane & 31, hf = lane >> 5;
+    const int g = blockIdx.x % a.Hk, y = blockIdx.x / a.Hk;
+    const int T = a.T;
+
+    const int qt = a.order[y];
+    const int R = w * 32 + l32;
+    const int head = g * a.G + (R >> a.lgBMq);
+    const int pos = qt * a.BMq + (R & (a.BMq - 1));
+    const int lb = a.ptr[qt], le = a.ptr[qt + 1];
+    const bool row_ok = pos < T;
+    const int n = le - lb;
+
+    f32x16 acc[4];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+    float m2 = -INFINITY, lsum = 0.f;
+
+    // Q row fragments: B operand, lane holds dims 16*ks + 8*hf .. +7 of its row.
+    bf16x8 qf[8];
+    {
+        const bf16* qp = a.q + ((size_t)min(pos, T - 1) * a.Hq + head) * HEAD_DIM + 8 * hf;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) qf[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 16 * ks));
+    }
+
+    const bf16* kbase = a.k + (size_t)g * HEAD_DIM;
+    const bf16* vbase = a.v + (size_t)g * HEAD_DIM;
+    const size_t kv_row = (size_t)a.Hk * HEAD_DIM;
+
+    EntryStream es;
+    es.init(a.ent, lb, n, lane);
+    int e_cur = 0, e_nxt = 0;   // entries of tiles t and t + 1
+
+    // Rows past the end are read from row T - 1 (finite data; such keys are masked).
+    u32x4 kreg[CPT], vreg[CPT];
+    int4 dreg = {0, 0, 0, 0};
+    bool dzero = false;
+    auto load_tile = [&](int t) {
+        const int e = es.get(t, lane);
+        e_cur = e_nxt;
+        e_nxt = e;
+        const int key0 = (e >> 1) * FWD_BN;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = tid + i * NT, key = min(key0 + (c >> 4), T - 1);
+            const size_t o = (size_t)key * kv_row + (c & 15) * 8;
+            kreg[i] = *reinterpret_cast<const u32x4*>(kbase + o);
+            vreg[i] = *reinterpret_cast<const u32x4*>(vbase + o);
+        }
+        if (tid < FWD_BN) {
+            const int key = key0 + tid;
+            dreg = a.desc[min(key, T - 1)];
+            dzero = key >= T;
+        }
+    };
+    auto store_tile = [&](int slot) {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = tid + i * NT, row = c >> 4, col = (c & 15) * 8;
+            *reinterpret_cast<u32x4*>(&Kb[slot][row * K_LD + col]) = kreg[i];
+            *reinterpret_cast<u32x4*>(&Vb[slot][row * V_LD + col]) = vreg[i];
+        }
+        if (tid < FWD_BN) Db[slot][tid] = dzero ? int4{0, 0, 0, 0} : dreg;
+    };
+
+    if (n > 0) {
+        load_tile(0);
+        store_tile(0);
+        if (n > 1) load_tile(1);
+    }
+    lds_barrier();
+
+    for (int t = 0; t < n; ++t) {
+        const int cb = t & 1;
+        const int e = t + 1 < n ? e_cur : e_nxt;
+        const int key0 = (e >> 1) * FWD_BN;
+        const bool need_mask = (e & 1) == 0 || key0 + FWD_BN > T;
+
+        // S^T = K Q^T for the two 32-key halves of the tile
+        f32x16 s[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+        const bf16* kr = Kb[cb] + l32 * K_LD + 8 * hf;
+        mfma_pipelined<16>(
+            [&](int i) { return *reinterpret_cast<const u32x4*>(kr + (i & 1) * 32 * K_LD + 16 * (i >> 1)); },
+            [&](int i, u32x4 op) { s[i & 1] = mfma32(as_bf16x8(op), qf[i >> 1], s[i & 1]); });
+
+        if (need_mask) {
+            const int4* dbuf = Db[cb];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int4 d = dbuf[kb * 32 + acc_row(r, hf)];
+                    const bool vis = ((unsigned)(pos - d.x) < (unsigned)(d.y - d.x)) |
+                                     ((unsigned)(pos - d.z) < (unsigned)(d.w - d.z));
+                    s[kb][r] = vis ? s[kb][r] : -INFINITY;
+                }
+        }
+
+        // online softmax (base 2), lazy rescale
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kb][r], s[kb][r + 1]));
+        if (__ballot(mx * a.c > m2 + RESCALE_SLACK) != 0ull) {
+            mx = fmaxf(mx, swap_halves(mx));
+            const float mnew = fmaxf(m2, mx * a.c);
+            const float alpha = (m2 == -INFINITY) ? 0.f : fast_exp2(m2 - mnew);
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
+            lsum *= alpha;
+            m2 = mnew;
+        }
+        const float msub = (m2 == -INFINITY) ? 0.f : m2;
+
+        bf16x8 pb[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            u32x4 pk;
+#pragma unroll
+            for (int e2 = 0; e2 < 8; e2 += 2) {
+                const float p0 = fast_exp2(fmaf(s[kk >> 1][(kk & 1) * 8 + e2], a.c, -msub));
+                const float p1 = fast_exp2(fmaf(s[kk >> 1][(kk & 1) * 8 + e2 + 1], a.c, -msub));
+                lsum += p0 + p1;
+                pk[e2 >> 1] = pack_bf16(p0, p1);
+            }
+            pb[kk] = as_bf16x8(pk);
+        }
+
+        // O^T += V^T P^T: key slot (hf, e) of step kk is key 16*kk + 8*(e/4) + 4*hf + e%4.
+        const bf16* vt = Vb[cb];
+        mfma_pipelined<16>(
+            [&](int i) {
+                const int kk = i >> 2, db = i & 3;
+                return tr_rows_ld(vt, V_LD, 16 * kk + 4 * hf, 16 * kk + 8 + 4 * hf, db * 32, lane);
+            },
+            [&](int i, u32x4 op) { acc[i & 3] = mfma32(as_bf16x8(op), pb[i >> 2], acc[i & 3]); });
+
+        // tile t + 1 into the other slot (its readers of tile t - 1 passed the last
+        // barrier), loads of tile t + 2
+        if (t + 1 < n) store_tile(cb ^ 1);
+        if (t + 2 < n) load_tile(t + 2);
+        lds_barrier();
+    }
+
+    const float ltot = lsum + swap_halves(lsum);
+    if (row_ok) {
+        const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+        bf16* op = a.o + ((size_t)pos * a.Hq + head) * HEAD_DIM;
+        bf16* olp = a.o_lo ? a.o_lo + ((size_t)pos * a.Hq + head) * HEAD_DIM : nullptr;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4) {
+                const int d0 = db * 32 + 8 * i4 + 4 * hf;
+                const float v0 = acc[db][4 * i4 + 0] * inv, v1 = acc[db][4 * i4 + 1] * inv;
+                const float v2 = acc[db][4 * i4 + 2] * inv, v3 = acc[db][4 * i4 + 3] * inv;
+                u32x2 pk;
+                pk[0] = pack_bf16(v0, v1);
+                pk[1] = pack_bf16(v2, v3);
+                *reinterpret_cast<u32x2*>(op + d0) = pk;
+                if (olp) {
+                    u32x2 lo;
+                    lo[0] = pack_bf16(v0 - bf16_lo(pk[0]), v1 - bf16_hi(pk[0]));
+                    lo[1] = pack_bf16(v2 - bf16_lo(pk[1]), v3 - bf16_hi(pk[1]));
+                    *reinterpret_cast<u32x2*>(olp + d0) = lo;
+                }
+            }
+        if (hf == 0)
+            a.lse[(size_t)head * T + pos] = ltot > 0.f ? (m2 + fast_log2(ltot)) * LN2 : -INFINITY;
+    }
+}
+
 hipError_t launch_fwd(const Problem& P, const void* q, const void* k, const void* v, void* o, void* o_lo,
                       float* lse, const int4* desc, const void* index, hipStream_t s) {
     const IndexLayout L = index_layout(P);
@@ -294,11 +511,12 @@ hipError_t launch_fwd(const Problem& P, const void* q, const void* k, const void
     a.Hk = P.Hk;
     a.G = P.G;
     a.BMq = P.fBM;
+    a.lgBMq = P.lgBM;
     a.nb = P.nb;
     a.sblock = P.sblock;
     a.c = P.scale * LOG2E;
     if (!P.sparse) {
-        hipLaunchKernelGGL((fwd_kernel<8, false>), dim3(P.Hk * P.nqt_f), dim3(512), 0, s, a);
+        hipLaunchKernelGGL(fwd_dense_kernel, dim3(P.Hk * P.nqt_f), dim3(512), 0, s, a);
     } else if (P.sblock == 64) {
         hipLaunchKernelGGL((fwd_kernel<2, true>), dim3(P.Hk * P.G * P.nb), dim3(128), 0, s, a);
     } else {
