@@ -1,17 +1,18 @@
 // Masked attention forward for gfx950.
 //
 // Work item = one workgroup = 32 * NW (head, position) rows that walk the same list of
-// 64-key tiles. Dense masks: the rows are the G query heads of one KV head times
-// 256/G consecutive positions (one query tile of the tile index), so every K/V tile
-// staged in LDS is reused by the whole GQA group. Block-sparse: the rows are one
-// (query head, query block) row of the keep matrix.
+// 64-key tiles. Dense masks (fwd_dense_kernel, NW = 8): the rows are the G query heads
+// of one KV head times 256/G consecutive positions (one query tile of the tile index),
+// so every K/V tile staged in LDS is reused by the whole GQA group. Block-sparse
+// (fwd_sparse_kernel, NW = b/32): the rows are one (query head, query block) row of the
+// keep matrix.
 //
 // Each wave owns 32 rows and computes the transposed scores S^T = K Q^T with
 // v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = Q held in registers), so a lane holds
 // one query row and 16 keys per 32-key block: the row max and row sum are mostly
 // in-lane, with one exchange between the two wave halves. The probabilities P^T then
-// feed O^T += V^T P^T directly as the B operand (no register shuffles); V is stored
-// transposed in LDS for the A operand.
+// feed O^T += V^T P^T directly as the B operand (no register shuffles); the A operand
+// V^T comes from LDS.
 //
 // Per tile: EMPTY tiles are not in the list; FULL tiles skip all mask work; PARTIAL
 // tiles (and the ragged last tile) test each element against the key's two visible row
@@ -42,16 +43,18 @@ struct FwdArgs {
     float c;   // scale * log2(e)
 };
 
-template <int NW, bool SPARSE>
-__global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
+// Block-sparse work items: one (query head, query block) row of the keep matrix, b/32
+// waves, each list entry a b-key block walked as b/64 tiles. K is staged in padded rows,
+// V transposed, single-buffered with two barriers per tile.
+template <int NW>
+__global__ __launch_bounds__(NW * 64) void fwd_sparse_kernel(FwdArgs a) {
     constexpr int NT = NW * 64;
     constexpr int KCH = 1024 / NT;   // 16-byte K chunks per thread per tile
     constexpr int VUN = 512 / NT;    // (key pair, 8 dims) V units per thread per tile
-    constexpr int TPE = SPARSE ? NW / 2 : 1;   // 64-key tiles per list entry
+    constexpr int TPE = NW / 2;   // 64-key tiles per list entry
 
     __shared__ __attribute__((aligned(16))) bf16 Ks[FWD_BN * KS_LD];
     __shared__ __attribute__((aligned(16))) bf16 Vt[HEAD_DIM * VT_LD];
-    __shared__ int4 Ds[FWD_BN];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int l32 = lane & 31, hf = lane >> 5;
@@ -60,22 +63,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
     const int g = blockIdx.x % a.Hk, y = blockIdx.x / a.Hk;
     const int T = a.T;
 
-    int head, pos, lb, le;
-    if constexpr (!SPARSE) {
-        const int qt = a.order[y];
-        const int R = w * 32 + l32;
-        head = g * a.G + R / a.BMq;
-        pos = qt * a.BMq + R % a.BMq;
-        lb = a.ptr[qt];
-        le = a.ptr[qt + 1];
-    } else {
-        const int hi = y / a.nb, qb = y - hi * a.nb;
-        head = g * a.G + hi;
-        pos = qb * a.sblock + w * 32 + l32;
-        const int r = head * a.nb + qb;
-        lb = a.ptr[r];
-        le = a.ptr[r + 1];
-    }
+    const int hi = y / a.nb, qb = y - hi * a.nb;
+    const int head = g * a.G + hi;
+    const int pos = qb * a.sblock + w * 32 + l32;
+    const int lb = a.ptr[head * a.nb + qb], le = a.ptr[head * a.nb + qb + 1];
     const bool row_ok = pos < T;
     const int ntiles = (le - lb) * TPE;
 
@@ -103,7 +94,6 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
     const size_t kv_row = (size_t)a.Hk * HEAD_DIM;
 
     u32x4 kreg[KCH], v0reg[VUN], v1reg[VUN];
-    int4 dreg = {0, 0, 0, 0};
     int nkey0 = 0;
     bool nmask = false;
 
@@ -111,15 +101,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
 #define FWD_LOAD_TILE(t)                                                                       \
     {                                                                                          \
         const int e_ = a.ent[lb + (t) / TPE];                                                  \
-        bool full_;                                                                            \
-        if constexpr (SPARSE) {                                                                \
-            nkey0 = e_ * a.sblock + ((t) % TPE) * FWD_BN;                                      \
-            full_ = true;                                                                      \
-        } else {                                                                               \
-            nkey0 = (e_ >> 1) * FWD_BN;                                                        \
-            full_ = (e_ & 1) != 0;                                                             \
-        }                                                                                      \
-        nmask = !full_ || nkey0 + FWD_BN > T;                                                  \
+        nkey0 = e_ * a.sblock + ((t) % TPE) * FWD_BN;                                          \
+        nmask = nkey0 + FWD_BN > T;                                                            \
         _Pragma("unroll") for (int i = 0; i < KCH; ++i) {                                      \
             const int c_ = tid + i * NT, key_ = nkey0 + (c_ >> 4);                             \
             u32x4 x_ = {0u, 0u, 0u, 0u};                                                       \
@@ -133,10 +116,6 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
             if (key_ + 1 < T) x1_ = *reinterpret_cast<const u32x4*>(vbase + (key_ + 1) * kv_row + d0_); \
             v0reg[i] = x0_;                                                                    \
             v1reg[i] = x1_;                                                                    \
-        }                                                                                      \
-        if (!SPARSE && nmask && tid < FWD_BN) {                                                \
-            const int key_ = nkey0 + tid;                                                      \
-            dreg = key_ < T ? a.desc[key_] : int4{0, 0, 0, 0};                                 \
         }                                                                                      \
     }
 
@@ -163,7 +142,6 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
                 *reinterpret_cast<uint32_t*>(&Vt[(d0 + 2 * m + 1) * VT_LD + 2 * p]) = (x0 >> 16) | (x1 & 0xffff0000u);
             }
         }
-        if (!SPARSE && need_mask && tid < FWD_BN) Ds[tid] = dreg;
         __syncthreads();
 
         if (t + 1 < ntiles) FWD_LOAD_TILE(t + 1);
@@ -185,15 +163,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int kk = kb * 32 + acc_row(r, hf);
-                    bool vis;
-                    if constexpr (SPARSE) {
-                        vis = key0 + kk < T;
-                    } else {
-                        const int4 d = Ds[kk];
-                        vis = (pos >= d.x && pos < d.y) || (pos >= d.z && pos < d.w);
-                    }
-                    if (!vis) s[kb][r] = -INFINITY;
+                    // the last tile of the sequence: keys past the end
+                    if (key0 + kb * 32 + acc_row(r, hf) >= T) s[kb][r] = -INFINITY;
                 }
         }
 
@@ -275,7 +246,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_kernel(FwdArgs a) {
 }
 
 // Dense work items (the G heads of one KV head x 256/G positions, 8 waves of 32 rows).
-// Same arithmetic as fwd_kernel, organised for fewer stalls:
+// Same arithmetic as fwd_sparse_kernel, organised for fewer stalls:
 //  - K, V and the column descriptors are double-buffered in LDS: while tile t is
 //    computed from slot t % 2, tile t + 1 (loaded one tile earlier) is stored into the
 //    other slot and the loads of tile t + 2 are issued; one barrier per tile;
@@ -518,9 +489,9 @@ hipError_t launch_fwd(const Problem& P, const void* q, const void* k, const void
     if (!P.sparse) {
         hipLaunchKernelGGL(fwd_dense_kernel, dim3(P.Hk * P.nqt_f), dim3(512), 0, s, a);
     } else if (P.sblock == 64) {
-        hipLaunchKernelGGL((fwd_kernel<2, true>), dim3(P.Hk * P.G * P.nb), dim3(128), 0, s, a);
+        hipLaunchKernelGGL((fwd_sparse_kernel<2>), dim3(P.Hk * P.G * P.nb), dim3(128), 0, s, a);
     } else {
-        hipLaunchKernelGGL((fwd_kernel<4, true>), dim3(P.Hk * P.G * P.nb), dim3(256), 0, s, a);
+        hipLaunchKernelGGL((fwd_sparse_kernel<4>), dim3(P.Hk * P.G * P.nb), dim3(256), 0, s, a);
     }
     return hipGetLastError();
 }
