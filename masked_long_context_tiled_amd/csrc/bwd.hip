@@ -237,28 +237,27 @@ __device__ __forceinline__ RowMap row_map(const BwdArgs& a, int g, int e) {
 // Work item: NWK blocks of 32 keys of one KV head, 2 * NWK waves. Waves 0..NWK-1 ("A")
 // compute S -> P and own dV^T; waves NWK..2*NWK-1 ("B") compute dP, receive P through LDS,
 // form dS and own dK^T. Wave w and w + NWK handle the same 32 keys and share a SIMD. All
-// products run on fp16 operands: Q, K, V, dO are multiplied by the powers of two sQ, sK,
-// sV, sO while being staged.
+// products run on fp16 operands (the preprocess's scaled copies of Q, K, V, dO).
 //
-// Each step handles 32 query rows in two halves separated by a barrier:
-//   1: A: S = Q K^T, P -> LDS and registers        B: dP = dO V^T
-//   2: A: dV^T += dO^T P                           B: dS = P * (dP - D), dK^T += Q^T dS
-//      then each role stages its tensor of the next step (A: Q and LSE, B: dO and D) into
-//      the other LDS buffer and issues the global loads of the step after that.
-// The staged rows are double-buffered: buffer s % 2 is read during step s only, and
-// buffer (s + 1) % 2 is written in the second half of step s, after every reader of
-// step s - 1 has passed the barrier that ended it. The two roles run separate loops with
-// the same two barriers per step.
+// The roles run one step apart, so a step (32 query rows) needs a single barrier:
+//   step s, A: S and P of step s + 1 (P -> LDS slot (s+1)%2 and registers),
+//              dV^T += dO_s^T P_s (P_s kept in registers from step s - 1),
+//              stage Q, LSE of step s + 2 into Q slot (s+2)%3, load step s + 3;
+//   step s, B: dP_s = dO_s V^T, dS_s = P_s * (dP_s - D_s) with P_s from LDS slot s%2,
+//              dK^T += Q_s^T dS_s, stage dO, D of step s + 1 into slot (s+1)%2, load s + 2.
+// Q_j is read in steps j - 1 (A) and j (B) and written in step j - 2, hence three slots;
+// dO_j and P_j are read in step j only and written in step j - 1, hence two. Every slot
+// is rewritten only after the barrier that ends the last step reading its old content.
 template <int NWK, bool SPARSE>
 __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
     constexpr int NR = NWK * 64;          // threads per role
     constexpr int KEYS = NWK * 32;
     constexpr int CPT = 512 / NR;         // 16-byte chunks per thread per staged row block
 
-    __shared__ __attribute__((aligned(16))) _Float16 Qh[2][32 * HEAD_DIM];    // swizzled rows
+    __shared__ __attribute__((aligned(16))) _Float16 Qh[3][32 * HEAD_DIM];    // swizzled rows
     __shared__ __attribute__((aligned(16))) _Float16 dOh[2][32 * HEAD_DIM];   // swizzled rows
-    __shared__ __attribute__((aligned(16))) _Float16 Ps[NWK * 2 * 64 * 8];    // [kb][kk][lane][8]
-    __shared__ __attribute__((aligned(16))) float lse_s[2][32];
+    __shared__ __attribute__((aligned(16))) _Float16 Ps[2][NWK * 2 * 64 * 8]; // [kb][kk][lane][8]
+    __shared__ __attribute__((aligned(16))) float lse_s[3][32];
     __shared__ __attribute__((aligned(16))) float dd_s[2][32];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -269,7 +268,6 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
     const int g = blockIdx.x % a.Hk, y = blockIdx.x / a.Hk;
     const int T = a.T;
 
-    // fp16 operand scales (powers of two) from the preprocess bounds
     const OperandScales sc = operand_scales(a.stats);
     const float sO = sc.sO, sQ = sc.sQ, sK = sc.sK, sV = sc.sV;
     const float cS = a.c / (sQ * sK);       // exponent scale for the scaled scores
@@ -304,23 +302,25 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
             kvf[ks] = as_f16x8(x);
         }
     }
+    int4 kd = {0, 0, 0, 0};
+    if (!SPARSE && is_a && key_ok) kd = a.desc[my_key];
 
     EntryStream es;
     es.init(a.ent, lb, le - lb, lane);
-    int e_cur = 0, e_nxt = 0;   // list entries of this step and the next
+    int e_q0 = 0, e_q1 = 0;   // A: list entries of the two most recently loaded steps
 
     // Staging of this role's tensor (A: Q and LSE, B: dO and D). Rows past the end are
     // read from a valid row and get LSE = +inf (P = 0) and D = 0 when stored.
     const _Float16* src = is_a ? a.qh : a.doh;
     const float* ssrc = is_a ? a.lse : a.dbuf;
+    const int span = SPARSE ? a.sblock : a.BMq;   // positions per list entry
     u32x4 pre[CPT];
     float praw = 0.f;
     bool pvalid = false;
-    const int span = SPARSE ? a.sblock : a.BMq;   // positions per list entry
     auto load_rows = [&](int st) {
         const int e = es.get(st >> lgRB, lane), rb = st & (RB - 1);
-        e_cur = e_nxt;
-        e_nxt = e;
+        e_q0 = e_q1;
+        e_q1 = e;
         const RowMap m = row_map<SPARSE>(a, g, e);
         if (m.pbase + span <= T) {
             // one base per step plus small per-lane offsets
@@ -345,8 +345,8 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
             praw = ssrc[(size_t)m.head(R) * T + min(p, T - 1)];
         }
     };
-    auto store_rows = [&](int buf) {
-        _Float16* dst = is_a ? Qh[buf] : dOh[buf];
+    auto store_rows = [&](int slot) {
+        _Float16* dst = is_a ? Qh[slot] : dOh[slot];
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const int c = rt + i * NR;
@@ -354,9 +354,61 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
         }
         if (rt < 32) {
             if (is_a)
-                lse_s[buf][rt] = (!pvalid || praw == -INFINITY) ? INFINITY : praw * LOG2E;
+                lse_s[slot][rt] = (!pvalid || praw == -INFINITY) ? INFINITY : praw * LOG2E;
             else
-                dd_s[buf][rt] = pvalid ? praw * sO : 0.f;
+                dd_s[slot][rt] = pvalid ? praw * sO : 0.f;
+        }
+    };
+
+    // A: S = Q K^T and P for step st (entry e) from Q slot qs; P -> LDS slot st % 2 and pb.
+    // P slots (hf, e) of 16-row step kk are rows 16*kk + 8*(e/4) + 4*hf + e%4.
+    auto s_and_p = [&](int st, int e, int qs, f16x8 (&pb)[2]) {
+        f32x16 sacc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
+        const _Float16* qh = Qh[qs];
+        mfma_pipelined<8>(
+            [&](int ks) { return *reinterpret_cast<const u32x4*>(&qh[swz_off(l32, 16 * ks + 8 * hf)]); },
+            [&](int ks, u32x4 op) { sacc = mfma32h(as_f16x8(op), kvf[ks], sacc); });
+        const bool full = SPARSE ? true : ((e & 1) != 0);
+        const bool all_vis = full && key_base + KEYS <= T;   // no element of the step masked
+        uint32_t vis = key_ok ? 0xffffu : 0u;
+        if (!full && key_ok) {
+            const RowMap rm = row_map<SPARSE>(a, g, e);
+            const int rb = st & (RB - 1);
+            vis = 0u;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int p = rm.pos(rb * 32 + acc_row(r, hf));
+                const bool v = (p >= kd.x && p < kd.y) || (p >= kd.z && p < kd.w);
+                vis |= (uint32_t)v << r;
+            }
+        }
+        _Float16* ps = Ps[st & 1];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            const float4 l0 = *reinterpret_cast<const float4*>(&lse_s[qs][16 * kk + 4 * hf]);
+            const float4 l1 = *reinterpret_cast<const float4*>(&lse_s[qs][16 * kk + 8 + 4 * hf]);
+            const float lr[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+            u32x4 pk;
+            if (all_vis) {
+#pragma unroll
+                for (int e2 = 0; e2 < 8; e2 += 2) {
+                    const int r0 = kk * 8 + e2;
+                    pk[e2 >> 1] = pack_f16(fast_exp2(fmaf(sacc[r0], cS, -lr[e2])),
+                                           fast_exp2(fmaf(sacc[r0 + 1], cS, -lr[e2 + 1])));
+                }
+            } else {
+#pragma unroll
+                for (int e2 = 0; e2 < 8; e2 += 2) {
+                    const int r0 = kk * 8 + e2, r1 = r0 + 1;
+                    const float p0 = fast_exp2(fmaf(sacc[r0], cS, -lr[e2]));
+                    const float p1 = fast_exp2(fmaf(sacc[r1], cS, -lr[e2 + 1]));
+                    pk[e2 >> 1] = pack_f16(((vis >> r0) & 1u) ? p0 : 0.f, ((vis >> r1) & 1u) ? p1 : 0.f);
+                }
+            }
+            pb[kk] = as_f16x8(pk);
+            *reinterpret_cast<u32x4*>(&ps[((kb * 2 + kk) * 64 + lane) * 8]) = pk;
         }
     };
 
@@ -366,82 +418,55 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
+    // prologue: A stages Q_0 and Q_1, B stages dO_0; A forms P_0; loads of Q_2 / dO_1
     if (nsteps > 0) {
-        load_rows(0);
-        store_rows(0);
-        if (nsteps > 1) load_rows(1);
+        if (is_a) {
+            load_rows(0);
+            store_rows(0);
+            if (nsteps > 1) {
+                load_rows(1);
+                store_rows(1);
+            }
+        } else {
+            load_rows(0);
+            store_rows(0);
+        }
     }
     lds_barrier();
-
-    // P and dS slots (hf, e) of 16-row step kk are rows 16*kk + 8*(e/4) + 4*hf + e%4.
-    if (is_a) {
-        int4 kd = {0, 0, 0, 0};
-        if (!SPARSE && key_ok) kd = a.desc[my_key];
+    f16x8 pb_cur[2];   // A: P of the step being finished
+    if (nsteps > 0 && is_a) {
         // settle the one-time loads here, so no step waits for them behind its prefetches
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        for (int step = 0; step < nsteps; ++step) {
-            const int cb = step & 1;
-            // S = Q K^T (scaled by sQ * sK); rows q = acc_row(r, hf)
-            f32x16 sacc;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
-            const _Float16* qh = Qh[cb];
-            mfma_pipelined<8>(
-                [&](int ks) { return *reinterpret_cast<const u32x4*>(&qh[swz_off(l32, 16 * ks + 8 * hf)]); },
-                [&](int ks, u32x4 op) { sacc = mfma32h(as_f16x8(op), kvf[ks], sacc); });
-            const int e = e_cur;
-            const bool full = SPARSE ? true : ((e & 1) != 0);
-            uint32_t vis = key_ok ? 0xffffu : 0u;
-            if (!full && key_ok) {
-                const RowMap rm = row_map<SPARSE>(a, g, e);
-                const int rb = step & (RB - 1);
-                vis = 0u;
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int p = rm.pos(rb * 32 + acc_row(r, hf));
-                    const bool v = (p >= kd.x && p < kd.y) || (p >= kd.z && p < kd.w);
-                    vis |= (uint32_t)v << r;
-                }
-            }
-            f16x8 pb[2];
-            const bool all_vis = full && key_base + KEYS <= T;   // no element of the step masked
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const float4 l0 = *reinterpret_cast<const float4*>(&lse_s[cb][16 * kk + 4 * hf]);
-                const float4 l1 = *reinterpret_cast<const float4*>(&lse_s[cb][16 * kk + 8 + 4 * hf]);
-                const float lr[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
-                u32x4 pk;
-                if (all_vis) {
-#pragma unroll
-                    for (int e2 = 0; e2 < 8; e2 += 2) {
-                        const int r0 = kk * 8 + e2;
-                        pk[e2 >> 1] = pack_f16(fast_exp2(fmaf(sacc[r0], cS, -lr[e2])),
-                                               fast_exp2(fmaf(sacc[r0 + 1], cS, -lr[e2 + 1])));
-                    }
-                } else {
-#pragma unroll
-                    for (int e2 = 0; e2 < 8; e2 += 2) {
-                        const int r0 = kk * 8 + e2, r1 = r0 + 1;
-                        const float p0 = fast_exp2(fmaf(sacc[r0], cS, -lr[e2]));
-                        const float p1 = fast_exp2(fmaf(sacc[r1], cS, -lr[e2 + 1]));
-                        pk[e2 >> 1] = pack_f16(((vis >> r0) & 1u) ? p0 : 0.f, ((vis >> r1) & 1u) ? p1 : 0.f);
-                    }
-                }
-                pb[kk] = as_f16x8(pk);
-                *reinterpret_cast<u32x4*>(&Ps[((kb * 2 + kk) * 64 + lane) * 8]) = pk;
-            }
-            lds_barrier();   // P of this step in LDS
+        s_and_p(0, nsteps > 1 ? e_q0 : e_q1, 0, pb_cur);   // loads so far: steps 0 and 1
+        if (nsteps > 2) load_rows(2);
+    }
+    if (nsteps > 1 && !is_a) load_rows(1);
+    lds_barrier();
 
-            // dV^T += (dO * sO)^T P
-            const _Float16* doh = dOh[cb];
+    if (is_a) {
+        // At the top of step s the last two loads were of steps s + 1 and s + 2 (e_q0, e_q1),
+        // or of steps s and s + 1 when s + 2 is past the end.
+        int qs1 = 1;   // Q slot of step s + 1
+        for (int step = 0; step < nsteps; ++step) {
+            f16x8 pb_next[2];
+            if (step + 1 < nsteps) s_and_p(step + 1, step + 2 < nsteps ? e_q0 : e_q1, qs1, pb_next);
+
+            // dV^T += (dO * sO)^T P of this step
+            const _Float16* doh = dOh[step & 1];
             mfma_pipelined<8>(
                 [&](int i) { return tr_rows_swz(doh, 16 * (i & 1) + 4 * hf, 16 * (i & 1) + 8 + 4 * hf, (i >> 1) * 32, lane); },
-                [&](int i, u32x4 op) { acc[i >> 1] = mfma32h(as_f16x8(op), pb[i & 1], acc[i >> 1]); });
-            if (step + 1 < nsteps) store_rows(cb ^ 1);
-            if (step + 2 < nsteps) load_rows(step + 2);
-            lds_barrier();   // end of step
+                [&](int i, u32x4 op) { acc[i >> 1] = mfma32h(as_f16x8(op), pb_cur[i & 1], acc[i >> 1]); });
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) pb_cur[kk] = pb_next[kk];
+
+            const int qs2 = qs1 == 2 ? 0 : qs1 + 1;   // Q slot of step s + 2
+            if (step + 2 < nsteps) store_rows(qs2);
+            if (step + 3 < nsteps) load_rows(step + 3);
+            qs1 = qs2;
+            lds_barrier();
         }
     } else {
+        int qs0 = 0;   // Q slot of step s
         for (int step = 0; step < nsteps; ++step) {
             const int cb = step & 1;
             // dP = dO V^T (scaled by sO * sV)
@@ -452,13 +477,13 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
             mfma_pipelined<8>(
                 [&](int ks) { return *reinterpret_cast<const u32x4*>(&doh[swz_off(l32, 16 * ks + 8 * hf)]); },
                 [&](int ks, u32x4 op) { dpacc = mfma32h(as_f16x8(op), kvf[ks], dpacc); });
-            lds_barrier();   // P of this step in LDS
 
             // dS * sO = P * (dP * sO - D * sO); dK^T += (Q * sQ)^T (dS * sO)
             f16x8 sb[2];
+            const _Float16* ps = Ps[cb];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
-                const f16x8 ph = as_f16x8(*reinterpret_cast<const u32x4*>(&Ps[((kb * 2 + kk) * 64 + lane) * 8]));
+                const f16x8 ph = as_f16x8(*reinterpret_cast<const u32x4*>(&ps[((kb * 2 + kk) * 64 + lane) * 8]));
                 const float4 d0v = *reinterpret_cast<const float4*>(&dd_s[cb][16 * kk + 4 * hf]);
                 const float4 d1v = *reinterpret_cast<const float4*>(&dd_s[cb][16 * kk + 8 + 4 * hf]);
                 const float dr[8] = {d0v.x, d0v.y, d0v.z, d0v.w, d1v.x, d1v.y, d1v.z, d1v.w};
@@ -478,13 +503,14 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
                 }
                 sb[kk] = sk;
             }
-            const _Float16* qh = Qh[cb];
+            const _Float16* qh = Qh[qs0];
             mfma_pipelined<8>(
                 [&](int i) { return tr_rows_swz(qh, 16 * (i & 1) + 4 * hf, 16 * (i & 1) + 8 + 4 * hf, (i >> 1) * 32, lane); },
                 [&](int i, u32x4 op) { acc[i >> 1] = mfma32h(as_f16x8(op), sb[i & 1], acc[i >> 1]); });
             if (step + 1 < nsteps) store_rows(cb ^ 1);
             if (step + 2 < nsteps) load_rows(step + 2);
-            lds_barrier();   // end of step
+            qs0 = qs0 == 2 ? 0 : qs0 + 1;
+            lds_barrier();
         }
     }
 
