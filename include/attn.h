@@ -68,6 +68,14 @@ typedef enum attn_status {
  *   CAUSAL_BLOCKWISE         j <= i && (i >= T - final_block_len || i / block_len == j / block_len)
  *   GLOBAL_SLIDING           i < global_len || j < global_len || |i - j| < window
  *   BLOCK_SPARSE             keep[h][i / b][j / b] != 0 (per query head h, b = sparse_block)
+ *   PREFIX_LM_DOCUMENT       doc(i) == doc(j) && (j - start(doc(j)) < prefix_len || j <= i):
+ *                            every document has its own bidirectional prefix of
+ *                            min(prefix_len, its length) positions, the rest causal
+ *   BLOCK_CAUSAL_DOCUMENT    doc(i) == doc(j) && blk(i) >= blk(j),
+ *                            blk(x) = (x - start(doc(x))) / block_len: blocks of block_len
+ *                            positions (restarting at every document, the last one of a
+ *                            document possibly shorter) see themselves fully and the
+ *                            earlier blocks of their document
  * Every kind except BLOCK_SPARSE is head-independent and has at most two visible row
  * intervals per key column, which is what the descriptor stores.
  */
@@ -82,21 +90,24 @@ typedef enum attn_mask_kind {
     ATTN_MASK_PREFIX_LM_CAUSAL = 7,
     ATTN_MASK_CAUSAL_BLOCKWISE = 8,
     ATTN_MASK_GLOBAL_SLIDING = 9,
-    ATTN_MASK_BLOCK_SPARSE = 10
+    ATTN_MASK_BLOCK_SPARSE = 10,
+    ATTN_MASK_PREFIX_LM_DOCUMENT = 11,
+    ATTN_MASK_BLOCK_CAUSAL_DOCUMENT = 12
 } attn_mask_kind;
 
 /* Mask parameters; fields a kind does not use are ignored. */
 typedef struct attn_mask_params {
     int32_t kind;             /* attn_mask_kind */
     int32_t window;           /* sliding window width w >= 1 */
-    int32_t prefix_len;       /* PREFIX_LM_CAUSAL: 0 <= prefix_len <= T */
+    int32_t prefix_len;       /* PREFIX_LM_CAUSAL: 0 <= prefix_len <= T; PREFIX_LM_DOCUMENT: >= 0 */
     int32_t question_len;     /* SHARED_QUESTION: T == question_len + n_answers * answer_len */
     int32_t answer_len;
     int32_t n_answers;
-    int32_t block_len;        /* CAUSAL_BLOCKWISE: block_len >= 1, 0 <= final_block_len <= T */
+    int32_t block_len;        /* CAUSAL_BLOCKWISE: block_len >= 1, 0 <= final_block_len <= T;
+                                 BLOCK_CAUSAL_DOCUMENT: block_len >= 1 */
     int32_t final_block_len;
     int32_t global_len;       /* GLOBAL_SLIDING: 0 <= global_len <= T, window >= 1 */
-    int32_t n_docs;           /* DOCUMENT kinds: number of documents >= 1 */
+    int32_t n_docs;           /* the four DOCUMENT kinds: number of documents >= 1 */
     const int32_t* cu_seqlens;/* host pointer, n_docs + 1 strictly increasing entries, 0 .. T */
 } attn_mask_params;
 

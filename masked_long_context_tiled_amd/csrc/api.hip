@@ -13,7 +13,7 @@ attn_status validate_problem(const attn_problem* p, Problem* out) {
     if (!p) return ATTN_ERR_INVALID_ARG;
     if (p->T < 1 || p->T > (1 << 24) || p->Hq < 1 || p->Hk < 1) return ATTN_ERR_INVALID_ARG;
     if (p->Hq % p->Hk != 0) return ATTN_ERR_INVALID_ARG;
-    if (p->mask_kind < ATTN_MASK_FULL || p->mask_kind > ATTN_MASK_BLOCK_SPARSE)
+    if (p->mask_kind < ATTN_MASK_FULL || p->mask_kind > ATTN_MASK_BLOCK_CAUSAL_DOCUMENT)
         return ATTN_ERR_INVALID_ARG;
     if (p->head_dim != HEAD_DIM) return ATTN_ERR_UNSUPPORTED;
     if (!(p->scale == p->scale) || isinf(p->scale)) return ATTN_ERR_INVALID_ARG;
@@ -157,6 +157,22 @@ static attn_status build_desc(const attn_mask_params* mp, int32_t T, int32_t* ou
         }
         return ATTN_OK;
     }
+    case ATTN_MASK_PREFIX_LM_DOCUMENT: {
+        const int32_t* cu = mp->cu_seqlens;
+        const long P = mp->prefix_len;
+        for (int d = 0; d < mp->n_docs; ++d)
+            for (int j = cu[d]; j < cu[d + 1]; ++j)   // prefix key: its whole document
+                put(j, j - cu[d] < P ? cu[d] : j, cu[d + 1], 0, 0);
+        return ATTN_OK;
+    }
+    case ATTN_MASK_BLOCK_CAUSAL_DOCUMENT: {
+        const int32_t* cu = mp->cu_seqlens;
+        const long b = mp->block_len;
+        for (int d = 0; d < mp->n_docs; ++d)
+            for (int j = cu[d]; j < cu[d + 1]; ++j)   // rows from the start of j's block on
+                put(j, (int)(cu[d] + (j - cu[d]) / b * b), cu[d + 1], 0, 0);
+        return ATTN_OK;
+    }
     default:
         return ATTN_ERR_INVALID_ARG;
     }
@@ -169,8 +185,12 @@ static attn_status validate_mask(const attn_mask_params* mp, int32_t T) {
     case ATTN_MASK_CAUSAL:
         return ATTN_OK;
     case ATTN_MASK_FULL_DOCUMENT:
-    case ATTN_MASK_CAUSAL_DOCUMENT: {
+    case ATTN_MASK_CAUSAL_DOCUMENT:
+    case ATTN_MASK_PREFIX_LM_DOCUMENT:
+    case ATTN_MASK_BLOCK_CAUSAL_DOCUMENT: {
         if (mp->n_docs < 1 || !mp->cu_seqlens) return ATTN_ERR_INVALID_ARG;
+        if (mp->kind == ATTN_MASK_PREFIX_LM_DOCUMENT && mp->prefix_len < 0) return ATTN_ERR_INVALID_ARG;
+        if (mp->kind == ATTN_MASK_BLOCK_CAUSAL_DOCUMENT && mp->block_len < 1) return ATTN_ERR_INVALID_ARG;
         const int32_t* cu = mp->cu_seqlens;
         if (cu[0] != 0 || cu[mp->n_docs] != T) return ATTN_ERR_INVALID_ARG;
         for (int d = 0; d < mp->n_docs; ++d)

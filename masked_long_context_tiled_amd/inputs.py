@@ -12,7 +12,7 @@ the GPU path uploads them as bf16.
 
 Source for the mask names and the problem shape: "LongCA-bench: 长上下文注意力基准测试"
 (xllm-io paper-review blog), section 三 "注意力掩码模式" (the 12 static masks and the
-two dynamic block masks) and section 四 "实验设置" (bf16, head dim 128, GQA 64:8 and
+two dynamic block masks; all but Variable Block are built here) and section 四 "实验设置" (bf16, head dim 128, GQA 64:8 and
 MHA 64:64, sequence length 1K-512K).
 """
 from __future__ import annotations
@@ -35,6 +35,8 @@ MASK_KINDS = (
     "causal_blockwise",
     "global_sliding",
     "block_sparse",
+    "prefix_lm_document",
+    "block_causal_document",
 )
 
 
@@ -43,14 +45,17 @@ class MaskSpec:
     """A mask kind and its parameters (positions are 0-based, in one packed sequence).
 
     window          sliding window width w (FULL/CAUSAL SLIDING WINDOW, GLOBAL SLIDING)
-    prefix_len      bidirectional prefix length (PREFIX LM CAUSAL)
+    prefix_len      bidirectional prefix length (PREFIX LM CAUSAL; per document for
+                    PREFIX LM DOCUMENT)
     question_len    shared question length (SHARED QUESTION)
     answer_len      length of each answer (SHARED QUESTION)
     n_answers       number of answers (SHARED QUESTION)
-    block_len       causal block length (CAUSAL BLOCKWISE)
+    block_len       causal block length (CAUSAL BLOCKWISE); block length within each
+                    document (BLOCK CAUSAL DOCUMENT)
     final_block_len length of the final block that sees everything before it (CAUSAL BLOCKWISE)
     global_len      number of global tokens at the start (GLOBAL SLIDING)
-    cu_seqlens      document boundaries, cu_seqlens[0] = 0, cu_seqlens[-1] = T (DOCUMENT masks)
+    cu_seqlens      document boundaries, cu_seqlens[0] = 0, cu_seqlens[-1] = T (the four
+                    DOCUMENT masks)
     sparse_block    block edge b of a uniform block-sparse mask (64 or 128)
     """
 
@@ -198,6 +203,12 @@ def workloads(seed: int = 0) -> dict:
         MaskSpec("causal_blockwise", block_len=1024, final_block_len=2048))
     w["global_sliding_16k"] = Workload("global_sliding_16k", 16384, 64, 8,
                                        MaskSpec("global_sliding", global_len=128, window=2048))
+    w["prefix_lm_document_32k"] = Workload("prefix_lm_document_32k", 32768, 64, 8,
+                                           MaskSpec("prefix_lm_document", prefix_len=1024,
+                                                    cu_seqlens=cu32))
+    w["block_causal_document_32k"] = Workload("block_causal_document_32k", 32768, 64, 8,
+                                              MaskSpec("block_causal_document", block_len=256,
+                                                       cu_seqlens=cu32))
     w["causal_128k"] = Workload("causal_128k", 131072, 64, 8, MaskSpec("causal"))
     for b in (128, 64):
         w[f"block_sparse_64k_b{b}"] = Workload(f"block_sparse_64k_b{b}", 65536, 64, 8,

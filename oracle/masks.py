@@ -5,7 +5,8 @@ Source: "LongCA-bench: 长上下文注意力基准测试" (xllm-io blog), sectio
 formulas; the predicates below are the plainest readings consistent with the names
 and with the workload descriptions (question + answers, bidirectional prefix,
 1024-token causal blocks with a final block that sees everything, 128 global tokens
-plus a window). i is the query position, j the key position, both 0-based in one
+plus a window; for the two document-level heterogeneous masks, the prefix and the
+causal blocks of the non-document versions applied inside every packed document). i is the query position, j the key position, both 0-based in one
 packed sequence of length T; h is the query head (only the block-sparse mask depends
 on it). ``visible`` is True where query i may attend to key j.
 """
@@ -66,6 +67,20 @@ def visible(spec, i, j, h=None, keep=None, T=None):
         # global tokens see and are seen by all; the rest see a window
         G = spec.global_len
         return (i < G) | (j < G) | (np.abs(i - j) < spec.window)
+    if k == "prefix_lm_document":
+        # per document: its first prefix_len positions bidirectional, the rest causal;
+        # nothing across documents
+        cu = np.asarray(spec.cu_seqlens, dtype=np.int64)
+        dj = _doc_of(cu, j)
+        same = _doc_of(cu, i) == dj
+        return same & (((j - cu[dj]) < spec.prefix_len) | (j <= i))
+    if k == "block_causal_document":
+        # per document: blocks of block_len positions (counted from the document start)
+        # see themselves fully and the earlier blocks of their document
+        cu = np.asarray(spec.cu_seqlens, dtype=np.int64)
+        di, dj = _doc_of(cu, i), _doc_of(cu, j)
+        b = spec.block_len
+        return (di == dj) & (((i - cu[di]) // b) >= ((j - cu[dj]) // b))
     if k == "block_sparse":
         # a (query block, key block) pair is visible iff kept for this head
         b = spec.sparse_block

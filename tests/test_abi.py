@@ -42,7 +42,7 @@ def test_problem_validation():
         (attn.problem(1024, 6, 2, "causal"), attn.ATTN_ERR_UNSUPPORTED),      # G = 3
         (attn.problem(1024, 8, 2, "causal", head_dim=64), attn.ATTN_ERR_UNSUPPORTED),
         (attn.problem(0, 8, 2, "causal"), attn.ATTN_ERR_INVALID_ARG),
-        (attn.problem(1024, 8, 2, 11), attn.ATTN_ERR_INVALID_ARG),            # unknown kind
+        (attn.problem(1024, 8, 2, 13), attn.ATTN_ERR_INVALID_ARG),            # unknown kind
         (attn.problem(1024, 8, 2, "block_sparse", 32), attn.ATTN_ERR_UNSUPPORTED),
         (attn.problem(1024, 512, 1, "causal"), attn.ATTN_ERR_UNSUPPORTED),    # G > 256
     ]
@@ -94,6 +94,9 @@ def test_mask_param_validation():
         (MaskSpec("causal_blockwise", block_len=0, final_block_len=8), 64),
         (MaskSpec("causal_blockwise", block_len=8, final_block_len=65), 64),
         (MaskSpec("block_sparse", sparse_block=64), 64),                 # no descriptor
+        (MaskSpec("prefix_lm_document", prefix_len=-1, cu_seqlens=(0, 64)), 64),
+        (MaskSpec("block_causal_document", block_len=0, cu_seqlens=(0, 64)), 64),
+        (MaskSpec("block_causal_document", block_len=4, cu_seqlens=(0, 70)), 64),  # does not end at T
     ]
     for spec, T in bad:
         with pytest.raises(attn.AttnError) as ei:
@@ -144,6 +147,12 @@ def _small_specs(T):
         MaskSpec("causal_blockwise", block_len=64, final_block_len=T),
         MaskSpec("global_sliding", global_len=16, window=40), MaskSpec("global_sliding", global_len=0, window=40),
         MaskSpec("global_sliding", global_len=60, window=30), MaskSpec("global_sliding", global_len=T, window=3),
+        MaskSpec("prefix_lm_document", prefix_len=30, cu_seqlens=document_cu_seqlens(6, T, 20, 200)),
+        MaskSpec("prefix_lm_document", prefix_len=0, cu_seqlens=document_cu_seqlens(7, T, 20, 200)),
+        MaskSpec("prefix_lm_document", prefix_len=10 * T, cu_seqlens=document_cu_seqlens(8, T, 20, 200)),
+        MaskSpec("block_causal_document", block_len=16, cu_seqlens=document_cu_seqlens(9, T, 20, 200)),
+        MaskSpec("block_causal_document", block_len=1, cu_seqlens=document_cu_seqlens(10, T, 20, 200)),
+        MaskSpec("block_causal_document", block_len=7 * T, cu_seqlens=document_cu_seqlens(11, T, 20, 200)),
     ]
 
 

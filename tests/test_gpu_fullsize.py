@@ -124,12 +124,13 @@ def test_8k(name):
 
 @pytest.mark.parametrize("name", ["full_document_32k", "causal_document_32k", "full_sliding_window_32k",
                                   "causal_sliding_window_32k", "shared_question_16k", "prefix_lm_causal_16k",
-                                  "causal_blockwise_16k", "global_sliding_16k"])
+                                  "causal_blockwise_16k", "global_sliding_16k", "prefix_lm_document_32k",
+                                  "block_causal_document_32k"])
 def test_workload_masks(name):
     wl, x, keep, out = _run(name)
     _check_rows(wl, x, keep, out, heads=[8, 15], rows=_sample_rows(wl.T, 24, 3))
     kind = wl.mask.kind
-    if kind in ("causal_document", "full_document"):
+    if kind in ("causal_document", "full_document", "prefix_lm_document", "block_causal_document"):
         cu = np.asarray(wl.mask.cu_seqlens)
         d = int(np.argmin(np.diff(cu)))                        # the shortest document
         _check_key_slab(wl, x, keep, out, 5, np.arange(cu[d], min(cu[d + 1], cu[d] + 64)))

@@ -51,10 +51,12 @@ def _specs_scaled(T):
         MaskSpec("prefix_lm_causal", prefix_len=250),
         MaskSpec("causal_blockwise", block_len=64, final_block_len=T - 12 * 64),
         MaskSpec("global_sliding", global_len=8, window=128),
+        MaskSpec("prefix_lm_document", prefix_len=70, cu_seqlens=document_cu_seqlens(5, T, 64, 400)),
+        MaskSpec("block_causal_document", block_len=48, cu_seqlens=document_cu_seqlens(6, T, 64, 400)),
     ]
 
 
-@pytest.mark.parametrize("idx", range(10))
+@pytest.mark.parametrize("idx", range(12))
 def test_every_interval_mask_gqa4_ragged(idx):
     T = 1000
     _check(T, 8, 2, _specs_scaled(T)[idx], seed=idx)
@@ -109,7 +111,7 @@ def test_block_sparse_mha_and_empty_rows():
 
 # --- tile index / block index: bit-exact ---------------------------------------------
 
-@pytest.mark.parametrize("idx", range(10))
+@pytest.mark.parametrize("idx", range(12))
 def test_tile_index_bit_exact(idx):
     T, Hq, Hk = 1000, 16, 2
     spec = _specs_scaled(T)[idx]

@@ -68,6 +68,17 @@ def _row_counts_intervals(spec, T):
             else:
                 lo, hi = max(G, i - w + 1), min(T, i + w)   # window part beyond the globals
                 n = G + max(0, hi - lo)
+        elif k == "prefix_lm_document":
+            cu = spec.cu_seqlens
+            d = max(x for x in range(len(cu) - 1) if cu[x] <= i)
+            Pd = min(spec.prefix_len, cu[d + 1] - cu[d])     # this document's prefix
+            n = max(Pd, i - cu[d] + 1)
+        elif k == "block_causal_document":
+            cu = spec.cu_seqlens
+            d = max(x for x in range(len(cu) - 1) if cu[x] <= i)
+            b = spec.block_len
+            end_of_block = cu[d] + ((i - cu[d]) // b + 1) * b
+            n = min(cu[d + 1], end_of_block) - cu[d]
         else:
             raise AssertionError(k)
         out[i] = n
@@ -77,7 +88,8 @@ def _row_counts_intervals(spec, T):
 @pytest.mark.parametrize("name", [
     "full_document_32k", "causal_document_32k", "full_sliding_window_32k",
     "causal_sliding_window_32k", "shared_question_16k", "prefix_lm_causal_16k",
-    "causal_blockwise_16k", "global_sliding_16k", "causal_8k_gqa", "full_8k_gqa"])
+    "causal_blockwise_16k", "global_sliding_16k", "causal_8k_gqa", "full_8k_gqa",
+    "prefix_lm_document_32k", "block_causal_document_32k"])
 def test_row_counts_at_workload_params(name):
     wl = workloads(0)[name]
     spec, T = wl.mask, wl.T
@@ -112,6 +124,25 @@ def test_U_closed_forms():
         == (F // b) * b * (b + 1) // 2 + (T * (T + 1) - F * (F + 1)) // 2
 
 
+def test_U_closed_forms_document_heterogeneous():
+    T = 4096
+    cu = document_cu_seqlens(5, T, 100, 900)
+    L = np.diff(cu).astype(np.int64)
+    P = 300
+    Pd = np.minimum(P, L)
+    # per document: the prefix block Pd x Pd, then row t >= Pd sees t + 1 keys
+    want = int((Pd * Pd + (L * (L + 1) - Pd * (Pd + 1)) // 2).sum())
+    assert visible_count(MaskSpec("prefix_lm_document", prefix_len=P, cu_seqlens=cu), T) == want
+    b = 64
+    # per document: block k (length m_k) sees the m_k keys of itself plus all earlier ones
+    tot = 0
+    for n in L:
+        starts = np.arange(0, n, b)
+        m = np.minimum(b, n - starts)
+        tot += int((m * (starts + m)).sum())
+    assert visible_count(MaskSpec("block_causal_document", block_len=b, cu_seqlens=cu), T) == tot
+
+
 def test_U_headline_causal_8k():
     # CAUSAL at T = 8192: T(T+1)/2 pairs per head
     assert visible_count(MaskSpec("causal"), 8192) == 33_558_528
@@ -130,6 +161,14 @@ def test_reductions():
     assert np.array_equal(_dense(MaskSpec("causal_blockwise", block_len=16, final_block_len=T), T), causal)
     assert np.array_equal(_dense(MaskSpec("full_document", cu_seqlens=(0, T)), T), full)
     assert np.array_equal(_dense(MaskSpec("causal_document", cu_seqlens=(0, T)), T), causal)
+    cu = (0, 20, 57, T)
+    fd, cd = _dense(MaskSpec("full_document", cu_seqlens=cu), T), _dense(MaskSpec("causal_document", cu_seqlens=cu), T)
+    assert np.array_equal(_dense(MaskSpec("prefix_lm_document", prefix_len=0, cu_seqlens=cu), T), cd)
+    assert np.array_equal(_dense(MaskSpec("prefix_lm_document", prefix_len=T, cu_seqlens=cu), T), fd)
+    assert np.array_equal(_dense(MaskSpec("prefix_lm_document", prefix_len=7, cu_seqlens=(0, T)), T),
+                          _dense(MaskSpec("prefix_lm_causal", prefix_len=7), T))
+    assert np.array_equal(_dense(MaskSpec("block_causal_document", block_len=1, cu_seqlens=cu), T), cd)
+    assert np.array_equal(_dense(MaskSpec("block_causal_document", block_len=T, cu_seqlens=cu), T), fd)
     w = 9
     assert np.array_equal(_dense(MaskSpec("global_sliding", global_len=0, window=w), T),
                           _dense(MaskSpec("full_sliding_window", window=w), T))
