@@ -31,7 +31,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from masked_long_context_tiled_amd import attn  # noqa: E402
-from masked_long_context_tiled_amd.inputs import attention_inputs, keep_for, workloads  # noqa: E402
+from masked_long_context_tiled_amd.inputs import MaskSpec, attention_inputs, keep_for, workloads  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0
@@ -105,6 +105,75 @@ def cpu_baseline(wl, x, keep, heads: int):
             "seconds": round(dt, 2)}
 
 
+def sweep(args, torch, dev):
+    """Forward + backward at T = 1K, 2K, ... --sweep-max for one mask at GQA 64:8, head dim
+    128: effective TFLOP/s and the peak device memory of each length (inputs, outputs,
+    tile index and workspace, as allocated by PyTorch's caching allocator). Inputs are
+    N(0,1) bf16 drawn on the device from a seeded generator."""
+    Hq, Hk, d = 64, 8, 128
+    spec = MaskSpec(args.sweep_mask)
+    points = []
+    T = 1024
+    while T <= args.sweep_max:
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        torch.cuda.reset_peak_memory_stats(dev)
+        base = torch.cuda.memory_allocated(dev)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(args.seed + T)
+        rnd = lambda *shape: torch.randn(*shape, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+        q, k, v, do = rnd(T, Hq, d), rnd(T, Hk, d), rnd(T, Hk, d), rnd(T, Hq, d)
+        prob = attn.problem(T, Hq, Hk, spec.kind)
+        idx_bytes = attn.tile_index_size(prob)
+        ws_bytes = attn.bwd_workspace_size(prob)
+        index = torch.empty(idx_bytes, dtype=torch.uint8, device=dev)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        o = torch.empty((T, Hq, d), dtype=torch.bfloat16, device=dev)
+        o_lo = torch.empty_like(o)
+        lse = torch.empty((Hq, T), dtype=torch.float32, device=dev)
+        dq = torch.empty((T, Hq, d), dtype=torch.float32, device=dev)
+        dk = torch.empty((T, Hk, d), dtype=torch.float32, device=dev)
+        dv = torch.empty((T, Hk, d), dtype=torch.float32, device=dev)
+        desc_host = attn.mask_desc_build(spec, T)
+        desc_dev = torch.from_numpy(desc_host).to(dev)
+        U, _ = visible_pairs(spec, T, desc_host, None)
+        fwd_flops = 4.0 * d * Hq * U
+        bwd_flops = 2.5 * fwd_flops
+        stream = torch.cuda.current_stream(dev)
+        sp = stream.cuda_stream
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+
+        def run():
+            attn.tile_index_build(prob, desc_dev.data_ptr(), index.data_ptr(), idx_bytes, sp)
+            ev[0].record(stream)
+            attn.fwd(prob, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), o_lo.data_ptr(),
+                     lse.data_ptr(), desc_dev.data_ptr(), index.data_ptr(), idx_bytes, 0, 0, sp)
+            ev[1].record(stream)
+            attn.bwd(prob, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), o_lo.data_ptr(),
+                     lse.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                     desc_dev.data_ptr(), index.data_ptr(), idx_bytes, ws.data_ptr(), ws_bytes, sp)
+            ev[2].record(stream)
+            ev[2].synchronize()
+            return ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2])
+
+        run()   # warm-up
+        reps = 3 if T <= 65536 else 1
+        tf, tb = zip(*[run() for _ in range(reps)])
+        t_f, t_b = float(np.median(tf)), float(np.median(tb))
+        peak = torch.cuda.max_memory_allocated(dev) - base
+        pt = {"T": T, "fwd_ms": round(t_f, 3), "bwd_ms": round(t_b, 3),
+              "fwd_tflops": round(fwd_flops / (t_f * 1e-3) / 1e12, 1),
+              "bwd_tflops": round(bwd_flops / (t_b * 1e-3) / 1e12, 1),
+              "peak_device_bytes": int(peak), "index_bytes": int(idx_bytes), "bwd_workspace_bytes": int(ws_bytes)}
+        points.append(pt)
+        log(f"sweep T={T}: fwd {pt['fwd_ms']} ms ({pt['fwd_tflops']} TF/s) bwd {pt['bwd_ms']} ms "
+            f"({pt['bwd_tflops']} TF/s) peak {peak / 2**30:.2f} GiB")
+        del q, k, v, do, index, ws, o, o_lo, lse, dq, dk, dv, desc_dev
+        T *= 2
+    print(json.dumps({"sweep": {"mask": spec.kind, "Hq": Hq, "Hk": Hk, "head_dim": d, "dtype": "bf16",
+                                "data": "synthetic", "seed": args.seed}, "points": points}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -115,6 +184,11 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=2, help="query heads in the oracle timing sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--out", default=None, help="also append the JSON line to this file")
+    ap.add_argument("--sweep", action="store_true",
+                    help="sequence-length sweep (1K .. --sweep-max, powers of two) of one mask at GQA 64:8: "
+                         "forward / backward TFLOP/s and peak device memory per length; prints one JSON line")
+    ap.add_argument("--sweep-mask", default="causal", choices=["causal", "full"])
+    ap.add_argument("--sweep-max", type=int, default=524288)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run attn_cast_bf16 over 2^28 floats 5 times (reads 1 GiB, writes 512 MiB "
                          "per launch): the known-size kernel that scales the HBM byte counters")
@@ -132,6 +206,10 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     attn.lib()   # fail loudly if the HIP library is missing
+
+    if args.sweep:
+        sweep(args, torch, dev)
+        return
 
     if args.copy_calibration:
         n = 1 << 28
