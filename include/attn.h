@@ -139,6 +139,49 @@ const char* attn_status_string(attn_status s);
 attn_status attn_mask_desc_build(const attn_mask_params* p, int32_t T, int32_t* desc_out);
 
 /*
+ * Context-parallel building block (the pages' ring / USP / LoongTrain methods exchange
+ * K/V chunks of one long sequence between devices and combine per-chunk results; see
+ * "LongCA-bench: 长上下文注意力基准测试", section 三 "分布式注意力机制" and section 四
+ * "分布式注意力性能"). A chunk pair is the n x n block of the global mask with query rows
+ * q_offset .. q_offset + n - 1 and key columns k_offset .. k_offset + n - 1 of a sequence
+ * of length T. Its descriptor, in chunk coordinates, turns the pair into an ordinary
+ * problem of length n: attn_tile_index_build / attn_fwd / attn_bwd run on it unchanged.
+ *   p        : mask parameters of the whole sequence (kind must not be BLOCK_SPARSE)
+ *   T        : global sequence length
+ *   q_offset, k_offset : global positions of the chunks' first query / key, >= 0,
+ *              q_offset + n <= T, k_offset + n <= T
+ *   n        : chunk length >= 1
+ *   desc_out : host int32 [n][4]: for local key j, the local query rows i with
+ *              visible(q_offset + i, k_offset + j), as at most two half-open intervals;
+ *              written entirely on success, untouched on error
+ * The forward of a chunk pair gives the attention of the query chunk over that key chunk
+ * only (O normalised over it, LSE over it; a row with no visible key in the chunk gets
+ * O = 0, LSE = -inf); attn_lse_merge combines such partial results over key chunks. The
+ * backward of a chunk pair, given the merged O (and O_lo) and LSE of the whole rows,
+ * gives that pair's share of dQ (summed over key chunks) and of dK, dV (summed over query
+ * chunks).
+ */
+attn_status attn_mask_desc_build_chunk(const attn_mask_params* p, int32_t T, int32_t q_offset, int32_t k_offset,
+                                       int32_t n, int32_t* desc_out);
+
+/*
+ * Merge a partial attention result over another key set into an accumulated one, in
+ * place: with m = max(LSE, LSE_part), w = exp(LSE - m), w_part = exp(LSE_part - m),
+ *   O <- (w O + w_part O_part) / (w + w_part),   LSE <- m + ln(w + w_part)
+ * (a row with both LSEs -inf keeps O = 0, LSE = -inf). This is exactly the attention over
+ * the union of the key sets. Start the accumulator from the first chunk's result.
+ *   prob          : T = chunk length, Hq; the other fields are validated but unused
+ *   o, o_lo       : device bf16 [T][Hq][128] accumulated O and its optional bf16 residual
+ *                   (O + O_lo is the fp32 value; o_lo may be NULL: then treated as 0 and
+ *                   not written)
+ *   lse           : device fp32 [Hq][T] accumulated LSE (natural log)
+ *   o_part, o_part_lo, lse_part : the partial result, same layouts (o_part_lo may be NULL)
+ * Errors: ATTN_ERR_INVALID_ARG for a null required pointer or a bad problem.
+ */
+attn_status attn_lse_merge(const attn_problem* prob, void* o, void* o_lo, float* lse, const void* o_part,
+                           const void* o_part_lo, const float* lse_part, void* stream);
+
+/*
  * Tile index: per-tile classes (EMPTY / PARTIAL / FULL) and the lists of non-empty
  * tiles the kernels walk, for the tile shapes the kernels use for this problem. EMPTY
  * tiles are skipped, FULL tiles run without per-element mask work, PARTIAL tiles

@@ -91,6 +91,9 @@ _SIGS = {
     "attn_bwd_dkdv": (ctypes.c_int, [_PROB, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _SZ, _P]),
     "attn_bwd_dq": (ctypes.c_int, [_PROB, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _SZ, _P]),
     "attn_cast_bf16": (ctypes.c_int, [_P, _P, _SZ, _P]),
+    "attn_mask_desc_build_chunk": (ctypes.c_int, [ctypes.POINTER(attn_mask_params), ctypes.c_int32, ctypes.c_int32,
+                                                  ctypes.c_int32, ctypes.c_int32, _P]),
+    "attn_lse_merge": (ctypes.c_int, [_PROB, _P, _P, _P, _P, _P, _P, _P]),
 }
 
 _lib = None
@@ -234,17 +237,33 @@ def cast_bf16(src: int, dst: int, n: int, stream: int = 0):
     _check(lib().attn_cast_bf16(src, dst, n, stream), "attn_cast_bf16")
 
 
+def mask_desc_build_chunk(spec: MaskSpec, T: int, q_offset: int, k_offset: int, n: int) -> np.ndarray:
+    """Host descriptor int32 [n][4] of the n x n chunk pair at (q_offset, k_offset)."""
+    p, keep = mask_params(spec)
+    out = np.empty((n, 4), dtype=np.int32)
+    _check(lib().attn_mask_desc_build_chunk(ctypes.byref(p), int(T), int(q_offset), int(k_offset), int(n),
+                                            out.ctypes.data), "attn_mask_desc_build_chunk")
+    return out
+
+
+def lse_merge(prob, o, o_lo, lse, o_part, o_part_lo, lse_part, stream=0):
+    _check(lib().attn_lse_merge(ctypes.byref(prob), o, o_lo, lse, o_part, o_part_lo, lse_part, stream),
+           "attn_lse_merge")
+
+
 # --- PyTorch-allocated convenience object ----------------------------------------------
 
 class MaskedAttention:
     """Buffers and index for one (T, Hq, Hk, mask) problem on a CUDA/HIP device.
 
     PyTorch provides the memory and the stream; every computation is a library call.
-    q, k, v, do are bf16 tensors [T][H][128]; outputs are allocated here.
+    q, k, v, do are bf16 tensors [T][H][128]; outputs are allocated here. ``desc`` may give
+    a ready host descriptor int32 [T][4] (e.g. of a chunk pair, from mask_desc_build_chunk)
+    instead of the one of ``spec`` over the whole length T.
     """
 
     def __init__(self, T: int, Hq: int, Hk: int, spec: MaskSpec, keep=None, device="cuda",
-                 scale: float = 0.0):
+                 scale: float = 0.0, desc=None):
         import torch
         self.torch = torch
         self.T, self.Hq, self.Hk, self.spec = T, Hq, Hk, spec
@@ -265,7 +284,9 @@ class MaskedAttention:
             block_index_build(self.prob, self.keep.data_ptr(), self.index.data_ptr(), self.index_bytes,
                               self._stream())
         else:
-            d = mask_desc_build(spec, T)
+            d = mask_desc_build(spec, T) if desc is None else np.ascontiguousarray(desc, dtype=np.int32)
+            if d.shape != (T, 4):
+                raise ValueError(f"descriptor shape {d.shape}, expected ({T}, 4)")
             self.desc = torch.from_numpy(d).to(self.device)
             tile_index_build(self.prob, self.desc.data_ptr(), self.index.data_ptr(), self.index_bytes,
                              self._stream())

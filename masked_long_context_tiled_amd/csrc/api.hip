@@ -83,98 +83,102 @@ IndexLayout index_layout(const Problem& P) {
 // ---------------------------------------------------------------------------------
 // Column-interval descriptor: for key column j the visible query rows are
 // [a0, b0) U [a1, b1). Each case below restates the kind's rule from attn.h in
-// column form.
+// column form, for one column of a sequence of length T.
 // ---------------------------------------------------------------------------------
-static attn_status build_desc(const attn_mask_params* mp, int32_t T, int32_t* out) {
+static void column_intervals(const attn_mask_params* mp, int32_t T, int j, long iv[4]) {
     const int k = mp->kind;
-    auto put = [&](int j, int a0, int b0, int a1, int b1) {
-        if (a0 >= b0) { a0 = b0 = 0; }
-        if (a1 >= b1) { a1 = b1 = 0; }
-        if (a0 == b0 && a1 != b1) { a0 = a1; b0 = b1; a1 = b1 = 0; }
-        out[4 * j + 0] = a0;
-        out[4 * j + 1] = b0;
-        out[4 * j + 2] = a1;
-        out[4 * j + 3] = b1;
+    auto set = [&](long a0, long b0, long a1, long b1) {
+        iv[0] = a0;
+        iv[1] = b0;
+        iv[2] = a1;
+        iv[3] = b1;
     };
-    auto imin = [](long a, long b) { return (int)(a < b ? a : b); };
-    auto imax = [](long a, long b) { return (int)(a > b ? a : b); };
+    auto lmin = [](long a, long b) { return a < b ? a : b; };
+    auto lmax = [](long a, long b) { return a > b ? a : b; };
+    // document of j: cu[d] <= j < cu[d + 1]
+    auto doc_of = [&](int x) {
+        int lo = 0, hi = mp->n_docs - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) / 2;
+            if (mp->cu_seqlens[mid] <= x) lo = mid; else hi = mid - 1;
+        }
+        return lo;
+    };
     switch (k) {
-    case ATTN_MASK_FULL:
-        for (int j = 0; j < T; ++j) put(j, 0, T, 0, 0);
-        return ATTN_OK;
-    case ATTN_MASK_CAUSAL:
-        for (int j = 0; j < T; ++j) put(j, j, T, 0, 0);
-        return ATTN_OK;
+    case ATTN_MASK_FULL: set(0, T, 0, 0); return;
+    case ATTN_MASK_CAUSAL: set(j, T, 0, 0); return;
     case ATTN_MASK_FULL_DOCUMENT:
     case ATTN_MASK_CAUSAL_DOCUMENT: {
-        const int n = mp->n_docs;
-        const int32_t* cu = mp->cu_seqlens;
-        for (int d = 0; d < n; ++d)
-            for (int j = cu[d]; j < cu[d + 1]; ++j)
-                put(j, k == ATTN_MASK_FULL_DOCUMENT ? cu[d] : j, cu[d + 1], 0, 0);
-        return ATTN_OK;
+        const int d = doc_of(j);
+        const long s0 = mp->cu_seqlens[d], e0 = mp->cu_seqlens[d + 1];
+        set(k == ATTN_MASK_FULL_DOCUMENT ? s0 : j, e0, 0, 0);
+        return;
     }
     case ATTN_MASK_FULL_SLIDING_WINDOW: {
         const long w = mp->window;
-        for (int j = 0; j < T; ++j) put(j, imax(0, j - w + 1), imin(T, j + w), 0, 0);
-        return ATTN_OK;
+        set(lmax(0, j - w + 1), lmin(T, j + w), 0, 0);
+        return;
     }
-    case ATTN_MASK_CAUSAL_SLIDING_WINDOW: {
-        const long w = mp->window;
-        for (int j = 0; j < T; ++j) put(j, j, imin(T, j + w), 0, 0);
-        return ATTN_OK;
-    }
+    case ATTN_MASK_CAUSAL_SLIDING_WINDOW: set(j, lmin(T, (long)j + mp->window), 0, 0); return;
     case ATTN_MASK_SHARED_QUESTION: {
         const long Qn = mp->question_len, A = mp->answer_len;
-        for (int j = 0; j < T; ++j) {
-            if (j < Qn) put(j, j, T, 0, 0);                       // question key: every later row
-            else put(j, j, imin(T, Qn + ((j - Qn) / A + 1) * A), 0, 0);  // rest of its answer
-        }
-        return ATTN_OK;
+        if (j < Qn) set(j, T, 0, 0);                                   // question key: every later row
+        else set(j, lmin(T, Qn + ((j - Qn) / A + 1) * A), 0, 0);       // rest of its answer
+        return;
     }
-    case ATTN_MASK_PREFIX_LM_CAUSAL: {
-        const long P = mp->prefix_len;
-        for (int j = 0; j < T; ++j) put(j, j < P ? 0 : j, T, 0, 0);
-        return ATTN_OK;
-    }
+    case ATTN_MASK_PREFIX_LM_CAUSAL: set(j < mp->prefix_len ? 0 : j, T, 0, 0); return;
     case ATTN_MASK_CAUSAL_BLOCKWISE: {
         const long b = mp->block_len, F = (long)T - mp->final_block_len;
-        for (int j = 0; j < T; ++j) {
-            if (j >= F) { put(j, j, T, 0, 0); continue; }
-            const int bend = imin(T, (j / b + 1) * b);            // rows of j's own block
-            if (bend >= F) put(j, j, T, 0, 0);                    // touches the final block
-            else put(j, j, bend, (int)F, T);
-        }
-        return ATTN_OK;
+        if (j >= F) { set(j, T, 0, 0); return; }
+        const long bend = lmin(T, ((long)j / b + 1) * b);              // rows of j's own block
+        if (bend >= F) set(j, T, 0, 0);                                // touches the final block
+        else set(j, bend, F, T);
+        return;
     }
     case ATTN_MASK_GLOBAL_SLIDING: {
         const long Gl = mp->global_len, w = mp->window;
-        for (int j = 0; j < T; ++j) {
-            if (j < Gl) { put(j, 0, T, 0, 0); continue; }          // global key: every row
-            const int lo = imax(0, j - w + 1), hi = imin(T, j + w);
-            if (lo <= Gl) put(j, 0, imax(hi, Gl), 0, 0);          // window meets the global rows
-            else put(j, 0, (int)Gl, lo, hi);
-        }
-        return ATTN_OK;
+        if (j < Gl) { set(0, T, 0, 0); return; }                       // global key: every row
+        const long lo = lmax(0, j - w + 1), hi = lmin(T, j + w);
+        if (lo <= Gl) set(0, lmax(hi, Gl), 0, 0);                      // window meets the global rows
+        else set(0, Gl, lo, hi);
+        return;
     }
     case ATTN_MASK_PREFIX_LM_DOCUMENT: {
-        const int32_t* cu = mp->cu_seqlens;
-        const long P = mp->prefix_len;
-        for (int d = 0; d < mp->n_docs; ++d)
-            for (int j = cu[d]; j < cu[d + 1]; ++j)   // prefix key: its whole document
-                put(j, j - cu[d] < P ? cu[d] : j, cu[d + 1], 0, 0);
-        return ATTN_OK;
+        const int d = doc_of(j);
+        const long s0 = mp->cu_seqlens[d], e0 = mp->cu_seqlens[d + 1];
+        set(j - s0 < mp->prefix_len ? s0 : j, e0, 0, 0);               // prefix key: its whole document
+        return;
     }
     case ATTN_MASK_BLOCK_CAUSAL_DOCUMENT: {
-        const int32_t* cu = mp->cu_seqlens;
-        const long b = mp->block_len;
-        for (int d = 0; d < mp->n_docs; ++d)
-            for (int j = cu[d]; j < cu[d + 1]; ++j)   // rows from the start of j's block on
-                put(j, (int)(cu[d] + (j - cu[d]) / b * b), cu[d + 1], 0, 0);
-        return ATTN_OK;
+        const int d = doc_of(j);
+        const long s0 = mp->cu_seqlens[d], e0 = mp->cu_seqlens[d + 1], b = mp->block_len;
+        set(s0 + (j - s0) / b * b, e0, 0, 0);                          // rows from the start of j's block on
+        return;
     }
-    default:
-        return ATTN_ERR_INVALID_ARG;
+    default: set(0, 0, 0, 0); return;                                   // not reached: validated first
+    }
+}
+
+// Descriptor of the n x n chunk pair (query rows q_offset.., key columns k_offset..) of
+// a sequence of length T, in chunk coordinates: each global interval is clipped to the
+// query chunk and shifted; empty intervals become [0, 0) and a lone interval comes first.
+static void build_desc(const attn_mask_params* mp, int32_t T, int32_t q_offset, int32_t k_offset, int32_t n,
+                       int32_t* out) {
+    for (int jl = 0; jl < n; ++jl) {
+        long iv[4];
+        column_intervals(mp, T, k_offset + jl, iv);
+        long a0 = iv[0] - q_offset, b0 = iv[1] - q_offset, a1 = iv[2] - q_offset, b1 = iv[3] - q_offset;
+        a0 = a0 < 0 ? 0 : a0;
+        a1 = a1 < 0 ? 0 : a1;
+        b0 = b0 > n ? n : b0;
+        b1 = b1 > n ? n : b1;
+        if (a0 >= b0) { a0 = b0 = 0; }
+        if (a1 >= b1) { a1 = b1 = 0; }
+        if (a0 == b0 && a1 != b1) { a0 = a1; b0 = b1; a1 = b1 = 0; }
+        out[4 * jl + 0] = (int32_t)a0;
+        out[4 * jl + 1] = (int32_t)b0;
+        out[4 * jl + 2] = (int32_t)a1;
+        out[4 * jl + 3] = (int32_t)b1;
     }
 }
 
@@ -240,7 +244,28 @@ attn_status attn_mask_desc_build(const attn_mask_params* p, int32_t T, int32_t* 
     if (!desc_out) return ATTN_ERR_INVALID_ARG;
     attn_status st = validate_mask(p, T);
     if (st != ATTN_OK) return st;
-    return build_desc(p, T, desc_out);
+    build_desc(p, T, 0, 0, T, desc_out);
+    return ATTN_OK;
+}
+
+attn_status attn_mask_desc_build_chunk(const attn_mask_params* p, int32_t T, int32_t q_offset, int32_t k_offset,
+                                       int32_t n, int32_t* desc_out) {
+    if (!desc_out) return ATTN_ERR_INVALID_ARG;
+    attn_status st = validate_mask(p, T);
+    if (st != ATTN_OK) return st;
+    if (n < 1 || q_offset < 0 || k_offset < 0 || (long)q_offset + n > T || (long)k_offset + n > T)
+        return ATTN_ERR_INVALID_ARG;
+    build_desc(p, T, q_offset, k_offset, n, desc_out);
+    return ATTN_OK;
+}
+
+attn_status attn_lse_merge(const attn_problem* prob, void* o, void* o_lo, float* lse, const void* o_part,
+                           const void* o_part_lo, const float* lse_part, void* stream) {
+    Problem P;
+    attn_status st = validate_problem(prob, &P);
+    if (st != ATTN_OK) return st;
+    if (!o || !lse || !o_part || !lse_part) return ATTN_ERR_INVALID_ARG;
+    return hip_status(launch_lse_merge(P, o, o_lo, lse, o_part, o_part_lo, lse_part, (hipStream_t)stream));
 }
 
 attn_status attn_tile_index_size(const attn_problem* prob, size_t* bytes_out) {

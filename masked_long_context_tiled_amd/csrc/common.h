@@ -217,5 +217,7 @@ hipError_t launch_bwd_main(const Problem& P, const void* q, const void* k, const
                            const void* dout, float* dq, float* dk, float* dv, const int4* desc,
                            const void* index, const float* dbuf, int parts, hipStream_t s);
 hipError_t launch_cast_bf16(const float* in, void* out, size_t n, hipStream_t s);
+hipError_t launch_lse_merge(const Problem& P, void* o, void* o_lo, float* lse, const void* o_part,
+                            const void* o_part_lo, const float* lse_part, hipStream_t s);
 
 }  // namespace mlct
