@@ -4,7 +4,8 @@ This module holds no attention arithmetic. It only:
   * names the mask kinds and carries their parameters (``MaskSpec``),
   * draws the random tensors (Q, K, V, dO) and rounds them to bf16 bit patterns,
   * draws the random structure the workloads need (document lengths for the
-    packed-sequence masks, the keep matrix of a uniform block-sparse mask),
+    packed-sequence masks, the keep matrix of a uniform block-sparse mask, the grid
+    and keep matrix of a variable-block mask),
   * lists the workload configurations by name.
 
 Both sides consume the same bits: the oracle upcasts the bf16 patterns to fp64,
@@ -12,7 +13,7 @@ the GPU path uploads them as bf16.
 
 Source for the mask names and the problem shape: "LongCA-bench: 长上下文注意力基准测试"
 (xllm-io paper-review blog), section 三 "注意力掩码模式" (the 12 static masks and the
-two dynamic block masks; all but Variable Block are built here) and section 四 "实验设置" (bf16, head dim 128, GQA 64:8 and
+two dynamic block masks) and section 四 "实验设置" (bf16, head dim 128, GQA 64:8 and
 MHA 64:64, sequence length 1K-512K).
 """
 from __future__ import annotations
@@ -39,6 +40,10 @@ MASK_KINDS = (
     "block_causal_document",
 )
 
+# Variable Block: block-sparse over a grid of variable block sizes. The library runs it as
+# the uniform 64-block mask its grid expands to, so it has no kind of its own in the C enum.
+VARIABLE_BLOCK = "variable_block"
+
 
 @dataclass(frozen=True)
 class MaskSpec:
@@ -57,6 +62,8 @@ class MaskSpec:
     cu_seqlens      document boundaries, cu_seqlens[0] = 0, cu_seqlens[-1] = T (the four
                     DOCUMENT masks)
     sparse_block    block edge b of a uniform block-sparse mask (64 or 128)
+    row_offsets     variable-block grid: row block r is [row_offsets[r], row_offsets[r+1])
+    col_offsets     and column block c is [col_offsets[c], col_offsets[c+1]) (0 ... T)
     """
 
     kind: str
@@ -70,9 +77,11 @@ class MaskSpec:
     global_len: int = 0
     cu_seqlens: Tuple[int, ...] = field(default_factory=tuple)
     sparse_block: int = 0
+    row_offsets: Tuple[int, ...] = field(default_factory=tuple)
+    col_offsets: Tuple[int, ...] = field(default_factory=tuple)
 
     def __post_init__(self):
-        if self.kind not in MASK_KINDS:
+        if self.kind not in MASK_KINDS and self.kind != VARIABLE_BLOCK:
             raise ValueError(f"unknown mask kind {self.kind!r}")
 
     @property
@@ -159,6 +168,43 @@ def block_sparse_keep(seed: int, Hq: int, nqb: int, nkb: int) -> np.ndarray:
     order = np.argsort(keys, axis=2, kind="stable")[:, :, :n_keep]
     keep = np.zeros((Hq, nqb, nkb), dtype=np.uint8)
     np.put_along_axis(keep, order, 1, axis=2)
+    return keep
+
+
+def variable_block_grid(seed: int, T: int, unit: int = 64, max_units: int = 8) -> Tuple[int, ...]:
+    """Block edges 0 = o_0 < o_1 < ... < o_n = T of a variable-block grid.
+
+    Block sizes are unit * m with m uniform on 1 .. max_units, drawn one after another
+    from ``default_rng(seed)`` until they cover T; the last block is cut at T.
+    """
+    rng = np.random.default_rng(seed)
+    off = [0]
+    while off[-1] < T:
+        off.append(min(T, off[-1] + unit * int(rng.integers(1, max_units + 1))))
+    return tuple(off)
+
+
+def variable_block_keep(seed: int, Hq: int, row_offsets, col_offsets) -> np.ndarray:
+    """Keep matrix uint8 [Hq][n_row_blocks][n_col_blocks] of a variable-block mask.
+
+    For every (query head, row block) the column blocks are visited in a random order
+    (``default_rng(seed)``, one permutation per row) and kept until they cover at least
+    half of the T keys, so every row block sees about 50 % of the keys and at least one
+    block.
+    """
+    rng = np.random.default_rng(seed)
+    nr, nc = len(row_offsets) - 1, len(col_offsets) - 1
+    size = np.diff(np.asarray(col_offsets, dtype=np.int64))
+    T = int(col_offsets[-1])
+    keep = np.zeros((Hq, nr, nc), dtype=np.uint8)
+    for h in range(Hq):
+        for r in range(nr):
+            covered = 0
+            for c in rng.permutation(nc):
+                if covered * 2 >= T:
+                    break
+                keep[h, r, c] = 1
+                covered += int(size[c])
     return keep
 
 

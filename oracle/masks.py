@@ -6,7 +6,9 @@ formulas; the predicates below are the plainest readings consistent with the nam
 and with the workload descriptions (question + answers, bidirectional prefix,
 1024-token causal blocks with a final block that sees everything, 128 global tokens
 plus a window; for the two document-level heterogeneous masks, the prefix and the
-causal blocks of the non-document versions applied inside every packed document). i is the query position, j the key position, both 0-based in one
+causal blocks of the non-document versions applied inside every packed document; the two
+dynamic masks of section 三 "动态掩码", Uniform Block and Variable Block, as block-sparse
+keep matrices over a uniform grid and over a grid of variable block sizes). i is the query position, j the key position, both 0-based in one
 packed sequence of length T; h is the query head (only the block-sparse mask depends
 on it). ``visible`` is True where query i may attend to key j.
 """
@@ -24,7 +26,8 @@ def visible(spec, i, j, h=None, keep=None, T=None):
     """Boolean array visible(i, j) (broadcast over i and j; h is a scalar head index).
 
     spec : masked_long_context_tiled_amd.inputs.MaskSpec (only its fields are read)
-    keep : uint8 [Hq][nqb][nkb] keep matrix, block-sparse only
+    keep : uint8 [Hq][nqb][nkb] keep matrix, block-sparse only (for variable_block:
+           [Hq][n_row_blocks][n_col_blocks] over the spec's grid)
     T    : sequence length, needed by CAUSAL BLOCKWISE (its final block is the last
            ``final_block_len`` positions)
     """
@@ -85,6 +88,12 @@ def visible(spec, i, j, h=None, keep=None, T=None):
         # a (query block, key block) pair is visible iff kept for this head
         b = spec.sparse_block
         return keep[h][i // b, j // b].astype(bool)
+    if k == "variable_block":
+        # block-sparse over a grid of variable block sizes: row block r covers
+        # [row_offsets[r], row_offsets[r+1]), column block c [col_offsets[c], col_offsets[c+1])
+        rb = np.searchsorted(np.asarray(spec.row_offsets, dtype=np.int64), i, side="right") - 1
+        cb = np.searchsorted(np.asarray(spec.col_offsets, dtype=np.int64), j, side="right") - 1
+        return keep[h][rb, cb].astype(bool)
     raise ValueError(f"unknown mask kind {k!r}")
 
 
