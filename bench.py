@@ -6,6 +6,10 @@ already resident in HBM:
   column-interval descriptor (host) -> device copy -> tile index (classifier + lists)
   -> attn_fwd -> attn_bwd_preprocess (D = rowsum(dO*O), operand bounds)
   -> attn_bwd_dkdv (dK, dV) -> attn_bwd_dq (dQ).
+Block-sparse workloads replace the first two steps by the block index of a keep matrix
+uploaded once; dynamic block-sparse workloads select that keep matrix from Q and K
+(attn_block_select, TopK / TopP) in every step; the variable-block workload expands its
+grid to the uniform 64-block keep matrix once, on the host, before timing.
 The default workload is CAUSAL at T = 8192, 64 query heads sharing 8 KV heads, head
 dim 128, bf16 inputs N(0,1) from a seed.
 
@@ -94,8 +98,15 @@ def cpu_baseline(wl, x, keep, heads: int):
     g = hs[0] // G
     k = bf16_bits_to_f64(x["k"][:, g:g + 1])
     v = bf16_bits_to_f64(x["v"][:, g:g + 1])
-    sub_keep = None if keep is None else keep[hs]
     t0 = time.perf_counter()
+    if wl.select is not None:
+        # dynamic block-sparse: the oracle selects the sample heads' blocks itself
+        from oracle.select import block_scores, select_topk, select_topp
+        s = block_scores(q, k, wl.mask.sparse_block)
+        mode, val = wl.select
+        sub_keep = select_topk(s, int(val), True) if mode == "topk" else select_topp(s, float(val), True)
+    else:
+        sub_keep = None if keep is None else keep[hs]
     attention_backward(q, k, v, do, wl.mask, keep=sub_keep)
     dt = time.perf_counter() - t0
     U = sum(visible_count(wl.mask, wl.T, h, sub_keep) for h in range(len(hs)))
@@ -232,12 +243,27 @@ def main():
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
     q, k, v, do = up(x["q"]), up(x["k"]), up(x["v"]), up(x["do"])
+    keep_oracle = keep
+    if spec.kind == "variable_block":
+        keep = attn.variable_block_expand(T, Hq, spec.row_offsets, spec.col_offsets, keep)
+        spec = MaskSpec("block_sparse", sparse_block=64)
+    dynamic = wl.select is not None
     sparse = spec.kind == "block_sparse"
     prob = attn.problem(T, Hq, Hk, spec.kind, spec.sparse_block if sparse else 0)
     idx_bytes = attn.tile_index_size(prob)
     index = torch.empty(idx_bytes, dtype=torch.uint8, device=dev)
     desc_dev = torch.empty((T, 4), dtype=torch.int32, device=dev)
-    keep_dev = torch.from_numpy(keep).to(dev) if sparse else None
+    if dynamic:
+        nb = -(-T // spec.sparse_block)
+        keep_dev = torch.empty((Hq, nb, nb), dtype=torch.uint8, device=dev)
+        scores = torch.empty((Hq, nb, nb), dtype=torch.float32, device=dev)
+        sel_bytes = attn.block_select_workspace_size(prob)
+        sel_ws = torch.empty(sel_bytes, dtype=torch.uint8, device=dev)
+        mode, val = wl.select
+        sel_params = attn.block_select_params(mode, topk=int(val) if mode == "topk" else 0,
+                                              topp=float(val) if mode == "topp" else 0.0, keep_diagonal=True)
+    else:
+        keep_dev = torch.from_numpy(keep).to(dev) if sparse else None
     o = torch.empty((T, Hq, d), dtype=torch.bfloat16, device=dev)
     o_lo = torch.empty((T, Hq, d), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((Hq, T), dtype=torch.float32, device=dev)
@@ -249,22 +275,21 @@ def main():
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
 
-    desc_host = None if sparse else attn.mask_desc_build(spec, T)
-    U, U_all = visible_pairs(spec, T, desc_host, keep)
-    # block-sparse U differs per head: use the exact total over heads
-    fwd_flops = 4.0 * d * (U_all if U_all is not None else Hq * U)
-    bwd_flops = 2.5 * fwd_flops
-
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
-    times = {"index": [], "fwd": [], "bwd_pre": [], "bwd_dkdv": [], "bwd_dq": []}
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(7)]
+    times = {"select": [], "index": [], "fwd": [], "bwd_pre": [], "bwd_dkdv": [], "bwd_dq": []}
 
     def step(record: bool):
         if sparse:
+            ev[6].record(stream)
+            if dynamic:
+                attn.block_select(prob, sel_params, q.data_ptr(), k.data_ptr(), scores.data_ptr(),
+                                  keep_dev.data_ptr(), sel_ws.data_ptr(), sel_bytes, sp)
             ev[0].record(stream)
             attn.block_index_build(prob, keep_dev.data_ptr(), index.data_ptr(), idx_bytes, sp)
         else:
             dh = attn.mask_desc_build(spec, T)                     # a1 (host)
             desc_dev.copy_(torch.from_numpy(dh))                   # synchronous, 16 B per key
+            ev[6].record(stream)
             ev[0].record(stream)
             attn.tile_index_build(prob, desc_dev.data_ptr(), index.data_ptr(), idx_bytes, sp)   # a2
         ev[1].record(stream)
@@ -284,6 +309,7 @@ def main():
         ev[5].record(stream)
         if record:
             ev[5].synchronize()
+            times["select"].append(ev[6].elapsed_time(ev[0]))
             times["index"].append(ev[0].elapsed_time(ev[1]))
             times["fwd"].append(ev[1].elapsed_time(ev[2]))
             times["bwd_pre"].append(ev[2].elapsed_time(ev[3]))
@@ -291,9 +317,17 @@ def main():
             times["bwd_dq"].append(ev[4].elapsed_time(ev[5]))
 
     log(f"warmup {args.warmup} steps")
-    for _ in range(args.warmup):
+    for _ in range(max(1, args.warmup)):
         step(False)
     torch.cuda.synchronize()
+
+    desc_host = None if sparse else attn.mask_desc_build(spec, T)
+    if dynamic:
+        keep = keep_dev.cpu().numpy()   # the selection is the same in every step (fixed inputs)
+    U, U_all = visible_pairs(spec, T, desc_host, keep)
+    # block-sparse U differs per head: use the exact total over heads
+    fwd_flops = 4.0 * d * (U_all if U_all is not None else Hq * U)
+    bwd_flops = 2.5 * fwd_flops
 
     # timed region: exactly K steps, synchronised on both sides
     log(f"timing {args.steps} steps")
@@ -319,7 +353,7 @@ def main():
     dkdv_flops = 0.8 * bwd_flops
     dkdv_tf = dkdv_flops / (mean["bwd_dkdv"] * 1e-3) / 1e12
     value = (fwd_flops + bwd_flops) / (ms_per_step * 1e-3) / 1e12
-    log(f"step {ms_per_step:.3f} ms | index {med['index']:.3f} fwd {med['fwd']:.3f} "
+    log(f"step {ms_per_step:.3f} ms | select {med['select']:.3f} index {med['index']:.3f} fwd {med['fwd']:.3f} "
         f"bwd_pre {med['bwd_pre']:.3f} dkdv {med['bwd_dkdv']:.3f} dq {med['bwd_dq']:.3f} ms | "
         f"fwd {fwd_tf:.1f} TF/s bwd {bwd_tf:.1f} TF/s")
 
@@ -337,7 +371,9 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "mask": spec.kind, "T": T, "Hq": Hq, "Hk": Hk, "head_dim": d,
-                   "global_batch": 1, "seq_len": T, "parallelism": "none", "seed": args.seed},
+                   "global_batch": 1, "seq_len": T, "parallelism": "none", "seed": args.seed,
+                   **({"select": list(wl.select)} if dynamic else {}),
+                   **({"sparse_block": spec.sparse_block} if sparse else {})},
         "visible_pairs_per_head": U,
         "fwd": {"ms": round(med["fwd"], 4), "tflops": round(fwd_tf, 2),
                 "frac_peak": round(fwd_tf / PEAK_BF16_TFLOPS, 4)},
@@ -346,6 +382,7 @@ def main():
                 "preprocess_ms": round(med["bwd_pre"], 4), "dkdv_ms": round(med["bwd_dkdv"], 4),
                 "dq_ms": round(med["bwd_dq"], 4)},
         "index_build_ms": round(med["index"], 4),
+        **({"select_ms": round(med["select"], 4)} if dynamic else {}),
         "roofline": {"kernel": "bwd_kernel (attn_bwd_dkdv)", "bound": "mfma",
                      "achieved": round(dkdv_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(dkdv_tf / PEAK_BF16_TFLOPS, 4),
@@ -356,7 +393,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_heads} heads")
-        rec["cpu_baseline"] = cpu_baseline(wl, x, keep, args.cpu_heads)
+        rec["cpu_baseline"] = cpu_baseline(wl, x, keep_oracle, args.cpu_heads)
     else:
         rec["cpu_baseline"] = None
     line = json.dumps(rec)

@@ -8,8 +8,10 @@
  * benchmarked on "LongCA-bench: 长上下文注意力基准测试" (xllm-io paper-review blog):
  *   - section 三 "注意力掩码模式": the regular masks (FULL, CAUSAL, FULL/CAUSAL DOCUMENT
  *     over packed sequences, FULL/CAUSAL SLIDING WINDOW), the heterogeneous masks
- *     (SHARED QUESTION, PREFIX LM CAUSAL, CAUSAL BLOCKWISE, GLOBAL SLIDING) and the
- *     dynamic Uniform Block mask (block-sparse, fixed 64x64 or 128x128 blocks);
+ *     (SHARED QUESTION, PREFIX LM CAUSAL, CAUSAL BLOCKWISE, GLOBAL SLIDING, PREFIX LM
+ *     DOCUMENT, BLOCK CAUSAL DOCUMENT) and the
+ *     dynamic Uniform Block mask (block-sparse, fixed 64x64 or 128x128 blocks)
+ *     and Variable Block (variable block sizes), with a TopK / TopP block selector;
  *   - section 三 "稀疏注意力内核": block size 64 and 128, GQA and MHA, forward and
  *     backward (the capability matrix of the sparse kernels);
  *   - section 四 "实验设置": bf16, head dim 128, GQA 64:8 and MHA 64:64, long sequences.
@@ -232,6 +234,70 @@ attn_status attn_tile_index_build(const attn_problem* prob, const int32_t* desc_
  */
 attn_status attn_block_index_build(const attn_problem* prob, const uint8_t* keep_dev,
                                    void* index_dev, size_t index_bytes, void* stream);
+
+/*
+ * Dynamic block selection: the keep matrix of a block-sparse problem chosen from the
+ * inputs themselves. The pages list Uniform Block as a dynamic mask (section 三
+ * "注意力掩码模式", 动态掩码) and name TopK / TopP as the selection criterion of dynamic
+ * block-sparse attention (the review's remarks on the paper's limitations); they give no
+ * formula. The definition implemented here:
+ *   block score  s[h][qb][kb] = scale * mean_Q[h][qb] . mean_K[h / G][kb], where
+ *                mean_Q[h][qb] is the fp32 mean of the rows of query block qb of head h
+ *                (the last block of a ragged T averages the rows it has), likewise mean_K;
+ *   order        per (h, qb): block qb first if keep_diagonal, then the other blocks by
+ *                descending score, equal scores by ascending kb;
+ *   TOPK         keep the first min(topk, nb) blocks of the order;
+ *   TOPP         keep the shortest prefix of the order whose mass under
+ *                softmax_kb(s[h][qb][kb]) (natural exp, over all nb blocks) reaches topp.
+ * Scores are fp32 (each a sequential FMA chain over the head dimension); the TopP masses
+ * are fp32 sums, so a prefix whose mass lies within fp32 rounding of topp may end one
+ * block earlier or later than an exact computation would.
+ */
+typedef enum attn_select_mode { ATTN_SELECT_TOPK = 0, ATTN_SELECT_TOPP = 1 } attn_select_mode;
+typedef struct attn_block_select_params {
+    int32_t mode;             /* attn_select_mode */
+    int32_t topk;             /* TOPK: >= 1 (values above nb keep every block) */
+    float topp;               /* TOPP: 0 < topp <= 1 */
+    int32_t keep_diagonal;    /* nonzero: block (qb, qb) is always kept and counted first */
+} attn_block_select_params;
+
+/* Workspace bytes of attn_block_select (the fp32 block means of Q and K). */
+attn_status attn_block_select_workspace_size(const attn_problem* prob, size_t* bytes_out);
+
+/*
+ *   prob      : a BLOCK_SPARSE problem (T, Hq, Hk, scale, sparse_block b); nb = ceil(T / b)
+ *               must be <= 4096 (ATTN_ERR_UNSUPPORTED otherwise)
+ *   q, k      : device bf16 [T][Hq][128], [T][Hk][128]
+ *   scores    : device fp32 [Hq][nb][nb] output, the block scores
+ *   keep_out  : device uint8 [Hq][nb][nb] output (0 / 1), ready for attn_block_index_build
+ *   ws        : device workspace of attn_block_select_workspace_size bytes
+ * Errors: ATTN_ERR_INVALID_ARG for a non-BLOCK_SPARSE problem, a null pointer, an unknown
+ * mode, topk < 1 or topp outside (0, 1]; ATTN_ERR_WORKSPACE for a short workspace.
+ */
+attn_status attn_block_select(const attn_problem* prob, const attn_block_select_params* sp, const void* q,
+                              const void* k, float* scores, uint8_t* keep_out, void* ws, size_t ws_bytes,
+                              void* stream);
+
+/*
+ * Variable Block mask (section 三 "注意力掩码模式", 动态掩码: block-sparse with variable
+ * block sizes; no further definition on the pages). Row block r covers query positions
+ * [row_off[r], row_off[r+1]), column block c key positions [col_off[c], col_off[c+1]), and
+ *   visible(h, i, j) = keep_var[h][r(i)][c(j)] != 0.
+ * With every block edge on a multiple of 64, each 64 x 64 tile lies inside one block
+ * pair, so the mask is exactly the uniform 64-block mask this function writes (host,
+ * synchronous); upload it and run the problem as BLOCK_SPARSE with sparse_block = 64.
+ *   T          : sequence length
+ *   Hq         : query heads
+ *   row_off    : host int32 [n_rb + 1], 0 = row_off[0] < ... < row_off[n_rb] = T, the
+ *                interior edges multiples of 64 (likewise col_off, n_cb)
+ *   keep_var   : host uint8 [Hq][n_rb][n_cb]
+ *   keep_out   : host uint8 [Hq][nt][nt], nt = ceil(T / 64), written entirely on success
+ * Errors: ATTN_ERR_INVALID_ARG for null pointers, T out of range or edges that are not
+ * as stated (nothing is written then).
+ */
+attn_status attn_variable_block_expand(int32_t T, int32_t Hq, const int32_t* row_off, int32_t n_rb,
+                                       const int32_t* col_off, int32_t n_cb, const uint8_t* keep_var,
+                                       uint8_t* keep_out);
 
 /* Workspace bytes of attn_fwd / attn_bwd (0 means no workspace is needed). */
 attn_status attn_fwd_workspace_size(const attn_problem* prob, size_t* bytes_out);

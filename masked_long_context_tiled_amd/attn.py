@@ -16,7 +16,7 @@ from typing import Optional
 
 import numpy as np
 
-from .inputs import MASK_KINDS, MaskSpec
+from .inputs import MASK_KINDS, VARIABLE_BLOCK, MaskSpec
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libattn.so")
@@ -59,6 +59,18 @@ class attn_problem(ctypes.Structure):
     ]
 
 
+class attn_block_select_params(ctypes.Structure):
+    _fields_ = [
+        ("mode", ctypes.c_int32),
+        ("topk", ctypes.c_int32),
+        ("topp", ctypes.c_float),
+        ("keep_diagonal", ctypes.c_int32),
+    ]
+
+
+ATTN_SELECT_TOPK, ATTN_SELECT_TOPP = 0, 1
+
+
 class attn_index_layout(ctypes.Structure):
     _fields_ = [
         ("nqt_f", ctypes.c_int32), ("nkt_f", ctypes.c_int32),
@@ -94,6 +106,11 @@ _SIGS = {
     "attn_mask_desc_build_chunk": (ctypes.c_int, [ctypes.POINTER(attn_mask_params), ctypes.c_int32, ctypes.c_int32,
                                                   ctypes.c_int32, ctypes.c_int32, _P]),
     "attn_lse_merge": (ctypes.c_int, [_PROB, _P, _P, _P, _P, _P, _P, _P]),
+    "attn_block_select_workspace_size": (ctypes.c_int, [_PROB, ctypes.POINTER(_SZ)]),
+    "attn_block_select": (ctypes.c_int, [_PROB, ctypes.POINTER(attn_block_select_params), _P, _P, _P, _P, _P,
+                                         _SZ, _P]),
+    "attn_variable_block_expand": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32, _P,
+                                                  ctypes.c_int32, _P, _P]),
 }
 
 _lib = None
@@ -251,6 +268,39 @@ def lse_merge(prob, o, o_lo, lse, o_part, o_part_lo, lse_part, stream=0):
            "attn_lse_merge")
 
 
+def block_select_params(mode: str, topk: int = 0, topp: float = 0.0, keep_diagonal: bool = True):
+    m = {"topk": ATTN_SELECT_TOPK, "topp": ATTN_SELECT_TOPP}[mode]
+    return attn_block_select_params(m, int(topk), float(topp), 1 if keep_diagonal else 0)
+
+
+def block_select_workspace_size(prob) -> int:
+    n = _SZ(0)
+    _check(lib().attn_block_select_workspace_size(ctypes.byref(prob), ctypes.byref(n)),
+           "attn_block_select_workspace_size")
+    return n.value
+
+
+def block_select(prob, params, q, k, scores, keep, ws, ws_bytes, stream=0):
+    _check(lib().attn_block_select(ctypes.byref(prob), ctypes.byref(params), q, k, scores, keep, ws, ws_bytes,
+                                   stream), "attn_block_select")
+
+
+def variable_block_expand(T: int, Hq: int, row_offsets, col_offsets, keep_var: np.ndarray) -> np.ndarray:
+    """Host uint8 [Hq][nt][nt] (nt = ceil(T / 64)): the uniform 64-block keep matrix of a
+    variable-block mask whose edges are multiples of 64."""
+    ro = np.ascontiguousarray(row_offsets, dtype=np.int32)
+    co = np.ascontiguousarray(col_offsets, dtype=np.int32)
+    kv = np.ascontiguousarray(keep_var, dtype=np.uint8)
+    if kv.shape != (Hq, len(ro) - 1, len(co) - 1):
+        raise ValueError(f"keep_var shape {kv.shape}, expected {(Hq, len(ro) - 1, len(co) - 1)}")
+    nt = -(-T // 64)
+    out = np.empty((Hq, nt, nt), dtype=np.uint8)
+    _check(lib().attn_variable_block_expand(int(T), int(Hq), ro.ctypes.data, len(ro) - 1, co.ctypes.data,
+                                            len(co) - 1, kv.ctypes.data, out.ctypes.data),
+           "attn_variable_block_expand")
+    return out
+
+
 # --- PyTorch-allocated convenience object ----------------------------------------------
 
 class MaskedAttention:
@@ -259,13 +309,21 @@ class MaskedAttention:
     PyTorch provides the memory and the stream; every computation is a library call.
     q, k, v, do are bf16 tensors [T][H][128]; outputs are allocated here. ``desc`` may give
     a ready host descriptor int32 [T][4] (e.g. of a chunk pair, from mask_desc_build_chunk)
-    instead of the one of ``spec`` over the whole length T.
+    instead of the one of ``spec`` over the whole length T. Block-sparse masks take
+    ``keep`` (uint8 [Hq][nb][nb], numpy or a device tensor); a variable-block spec takes its
+    keep matrix over the spec's grid (numpy) and runs as the 64-block mask it expands to.
     """
 
     def __init__(self, T: int, Hq: int, Hk: int, spec: MaskSpec, keep=None, device="cuda",
                  scale: float = 0.0, desc=None):
         import torch
         self.torch = torch
+        if spec.kind == VARIABLE_BLOCK:
+            # runs as the uniform 64-block mask its grid expands to (host expansion)
+            if keep is None or isinstance(keep, torch.Tensor):
+                raise ValueError("variable_block needs its keep matrix as a host numpy array")
+            keep = variable_block_expand(T, Hq, spec.row_offsets, spec.col_offsets, keep)
+            spec = MaskSpec("block_sparse", sparse_block=64)
         self.T, self.Hq, self.Hk, self.spec = T, Hq, Hk, spec
         self.device = torch.device(device)
         if self.device.type == "cuda" and self.device.index is None:

@@ -268,6 +268,69 @@ attn_status attn_lse_merge(const attn_problem* prob, void* o, void* o_lo, float*
     return hip_status(launch_lse_merge(P, o, o_lo, lse, o_part, o_part_lo, lse_part, (hipStream_t)stream));
 }
 
+attn_status attn_block_select_workspace_size(const attn_problem* prob, size_t* bytes_out) {
+    Problem P;
+    attn_status st = validate_problem(prob, &P);
+    if (st != ATTN_OK) return st;
+    if (!bytes_out || !P.sparse) return ATTN_ERR_INVALID_ARG;
+    *bytes_out = select_workspace_bytes(P);
+    return ATTN_OK;
+}
+
+attn_status attn_block_select(const attn_problem* prob, const attn_block_select_params* sp, const void* q,
+                              const void* k, float* scores, uint8_t* keep_out, void* ws, size_t ws_bytes,
+                              void* stream) {
+    Problem P;
+    attn_status st = validate_problem(prob, &P);
+    if (st != ATTN_OK) return st;
+    if (!P.sparse || !sp || !q || !k || !scores || !keep_out || !ws) return ATTN_ERR_INVALID_ARG;
+    if (sp->mode == ATTN_SELECT_TOPK) {
+        if (sp->topk < 1) return ATTN_ERR_INVALID_ARG;
+    } else if (sp->mode == ATTN_SELECT_TOPP) {
+        if (!(sp->topp > 0.f && sp->topp <= 1.f)) return ATTN_ERR_INVALID_ARG;
+    } else {
+        return ATTN_ERR_INVALID_ARG;
+    }
+    if (P.nb > SEL_MAX_NB) return ATTN_ERR_UNSUPPORTED;
+    if (ws_bytes < select_workspace_bytes(P)) return ATTN_ERR_WORKSPACE;
+    return hip_status(launch_block_select(P, sp->mode, sp->topk < P.nb ? sp->topk : P.nb, sp->topp,
+                                          sp->keep_diagonal ? 1 : 0, q, k, scores, keep_out, ws,
+                                          (hipStream_t)stream));
+}
+
+// Block edges 0 = off[0] < off[1] < ... < off[n] = T, the interior ones multiples of 64.
+static bool valid_edges(const int32_t* off, int32_t n, int32_t T) {
+    if (!off || n < 1 || off[0] != 0 || off[n] != T) return false;
+    for (int32_t r = 0; r < n; ++r) {
+        if (off[r + 1] <= off[r]) return false;
+        if (r + 1 < n && off[r + 1] % 64 != 0) return false;
+    }
+    return true;
+}
+
+attn_status attn_variable_block_expand(int32_t T, int32_t Hq, const int32_t* row_off, int32_t n_rb,
+                                       const int32_t* col_off, int32_t n_cb, const uint8_t* keep_var,
+                                       uint8_t* keep_out) {
+    if (T < 1 || T > (1 << 24) || Hq < 1 || !keep_var || !keep_out) return ATTN_ERR_INVALID_ARG;
+    if (!valid_edges(row_off, n_rb, T) || !valid_edges(col_off, n_cb, T)) return ATTN_ERR_INVALID_ARG;
+    const int64_t nt = (T + 63) / 64;
+    if ((int64_t)Hq * nt * nt > (int64_t)INT32_MAX) return ATTN_ERR_UNSUPPORTED;
+    for (int32_t h = 0; h < Hq; ++h) {
+        int32_t r = 0;
+        for (int64_t qt = 0; qt < nt; ++qt) {
+            while (row_off[r + 1] <= qt * 64) ++r;   // the row block holding tile qt
+            const uint8_t* kv = keep_var + ((size_t)h * n_rb + r) * n_cb;
+            uint8_t* out = keep_out + ((size_t)h * nt + qt) * nt;
+            int32_t c = 0;
+            for (int64_t kt = 0; kt < nt; ++kt) {
+                while (col_off[c + 1] <= kt * 64) ++c;
+                out[kt] = kv[c] ? 1 : 0;
+            }
+        }
+    }
+    return ATTN_OK;
+}
+
 attn_status attn_tile_index_size(const attn_problem* prob, size_t* bytes_out) {
     Problem P;
     attn_status st = validate_problem(prob, &P);

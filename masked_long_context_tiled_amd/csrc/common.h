@@ -217,6 +217,10 @@ hipError_t launch_bwd_main(const Problem& P, const void* q, const void* k, const
                            const void* dout, float* dq, float* dk, float* dv, const int4* desc,
                            const void* index, const float* dbuf, int parts, hipStream_t s);
 hipError_t launch_cast_bf16(const float* in, void* out, size_t n, hipStream_t s);
+constexpr int SEL_MAX_NB = 4096;   // longest row of blocks the selection kernel sorts
+size_t select_workspace_bytes(const Problem& P);
+hipError_t launch_block_select(const Problem& P, int mode, int topk, float topp, int keep_diag, const void* q,
+                               const void* k, float* scores, uint8_t* keep, void* ws, hipStream_t s);
 hipError_t launch_lse_merge(const Problem& P, void* o, void* o_lo, float* lse, const void* o_part,
                             const void* o_part_lo, const float* lse_part, hipStream_t s);
 

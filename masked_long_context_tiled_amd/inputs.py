@@ -220,6 +220,9 @@ class Workload:
     Hk: int
     mask: MaskSpec
     d: int = 128
+    # dynamic block-sparse: the keep matrix is selected from Q and K in every step,
+    # ("topk", k) or ("topp", p), the diagonal block always kept
+    select: Optional[Tuple[str, float]] = None
 
 
 def workloads(seed: int = 0) -> dict:
@@ -259,11 +262,24 @@ def workloads(seed: int = 0) -> dict:
     for b in (128, 64):
         w[f"block_sparse_64k_b{b}"] = Workload(f"block_sparse_64k_b{b}", 65536, 64, 8,
                                                MaskSpec("block_sparse", sparse_block=b))
+    w["topk_sparse_64k_b128"] = Workload("topk_sparse_64k_b128", 65536, 64, 8,
+                                         MaskSpec("block_sparse", sparse_block=128), select=("topk", 256))
+    w["topp_sparse_64k_b128"] = Workload("topp_sparse_64k_b128", 65536, 64, 8,
+                                         MaskSpec("block_sparse", sparse_block=128), select=("topp", 0.5))
+    w["variable_block_64k"] = Workload(
+        "variable_block_64k", 65536, 64, 8,
+        MaskSpec(VARIABLE_BLOCK, row_offsets=variable_block_grid(seed, 65536),
+                 col_offsets=variable_block_grid(seed + 1, 65536)))
     return w
 
 
 def keep_for(workload: Workload, seed: int) -> Optional[np.ndarray]:
-    """The keep matrix for a block-sparse workload (None for other masks)."""
+    """The keep matrix of a block-sparse or variable-block workload (None for other masks
+    and for dynamic workloads, whose keep matrix is selected from the inputs)."""
+    if workload.select is not None:
+        return None
+    if workload.mask.kind == VARIABLE_BLOCK:
+        return variable_block_keep(seed, workload.Hq, workload.mask.row_offsets, workload.mask.col_offsets)
     if workload.mask.kind != "block_sparse":
         return None
     b = workload.mask.sparse_block

@@ -153,3 +153,62 @@ def test_block_sparse_64k(name):
     wl, x, keep, out = _run(name)
     _check_rows(wl, x, keep, out, heads=[16, 17], rows=_sample_rows(wl.T, 12, 5))
     _check_sums(wl, x, out)
+
+
+@pytest.mark.timeout(600)
+def test_variable_block_64k():
+    wl, x, keep, out = _run("variable_block_64k")
+    _check_rows(wl, x, keep, out, heads=[16, 17], rows=_sample_rows(wl.T, 12, 6))
+    _check_sums(wl, x, out)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["topk_sparse_64k_b128", "topp_sparse_64k_b128"])
+def test_dynamic_sparse_64k(name):
+    """Selection on the GPU at full size, then the block-sparse path on the selected blocks.
+    The oracle selects the checked heads' blocks itself from fp64 block scores; the GPU's
+    selection must agree with it there."""
+    import torch
+    from oracle.select import block_scores, select_topk, select_topp
+
+    wl = workloads(0)[name]
+    b = wl.mask.sparse_block
+    nb = -(-wl.T // b)
+    mode, val = wl.select
+    note(f"full size {name}: T={wl.T} Hq={wl.Hq} Hk={wl.Hk} b={b} select={wl.select}: inputs")
+    x = attention_inputs(0, wl.T, wl.Hq, wl.Hk)
+    q, k, v, do = (to_dev_bf16(x[n], torch) for n in ("q", "k", "v", "do"))
+    prob = attn.problem(wl.T, wl.Hq, wl.Hk, "block_sparse", b)
+    scores = torch.empty((wl.Hq, nb, nb), dtype=torch.float32, device="cuda")
+    keep_dev = torch.empty((wl.Hq, nb, nb), dtype=torch.uint8, device="cuda")
+    nws = attn.block_select_workspace_size(prob)
+    ws = torch.empty(nws, dtype=torch.uint8, device="cuda")
+    params = attn.block_select_params(mode, topk=int(val) if mode == "topk" else 0,
+                                      topp=float(val) if mode == "topp" else 0.0, keep_diagonal=True)
+    note(f"full size {name}: GPU selection, forward + backward")
+    attn.block_select(prob, params, q.data_ptr(), k.data_ptr(), scores.data_ptr(), keep_dev.data_ptr(),
+                      ws.data_ptr(), nws, torch.cuda.current_stream().cuda_stream)
+    ma = attn.MaskedAttention(wl.T, wl.Hq, wl.Hk, wl.mask, keep=keep_dev)
+    o, lse, o_lo = ma.forward(q, k, v)
+    dq, dk, dv = ma.backward(q, k, v, o, lse, do, o_lo=o_lo)
+    torch.cuda.synchronize()
+    out = {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
+
+    heads = [16, 17]
+    qh, kh, _, _, g = _group_arrays(x, wl, heads)
+    ref_s = block_scores(qh, kh, b)
+    gpu_s = scores[heads].cpu().numpy().astype(np.float64)
+    err = float(np.abs(gpu_s - ref_s).max())
+    assert err <= 1e-5, f"block scores: max |err| = {err:.2e}"
+    keep_or = select_topk(ref_s, int(val), True) if mode == "topk" else select_topp(ref_s, float(val), True)
+    gpu_keep = keep_dev[heads].cpu().numpy()
+    same = (gpu_keep == keep_or).all(axis=2)                 # [2][nb] rows that agree
+    note(f"  scores max |err| {err:.2e}; selected rows equal to the oracle's: {same.sum()} of {same.size}")
+    assert same.mean() > 0.99
+    # attention rows in query blocks where both selections agree, with the oracle's keep
+    rows = _sample_rows(wl.T, 16, 7)
+    rows = rows[same.all(axis=0)[rows // b]]
+    keep_full = np.zeros((wl.Hq, nb, nb), dtype=np.uint8)
+    keep_full[heads] = keep_or
+    _check_rows(wl, x, keep_full, out, heads=heads, rows=rows)
+    _check_sums(wl, x, out)
