@@ -298,7 +298,7 @@ __global__ __launch_bounds__(512) void fwd_dense_kernel(FwdArgs a) {
     for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
-    float m2 = -INFINITY, lsum = 0.f;
+    float m2 = -INFINITY, lsum[2] = {0.f, 0.f};
 
     // Q row fragments: B operand, lane holds dims 16*ks + 8*hf .. +7 of its row.
     bf16x8 qf[8];
@@ -306,6 +306,11 @@ __global__ __launch_bounds__(512) void fwd_dense_kernel(FwdArgs a) {
         const bf16* qp = a.q + ((size_t)min(pos, T - 1) * a.Hq + head) * HEAD_DIM + 8 * hf;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) qf[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 16 * ks));
+        // Complete the Q loads here. Left pending into the loop, the wait the compiler puts
+        // before the first MFMAs that read Q also covers every K/V prefetch issued behind
+        // them, so each tile would stall on the next tile's loads.
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(as_u32x4(qf[ks])));
     }
 
     const bf16* kbase = a.k + (size_t)g * HEAD_DIM;
@@ -385,12 +390,14 @@ __global__ __launch_bounds__(512) void fwd_dense_kernel(FwdArgs a) {
                 }
         }
 
-        // online softmax (base 2), lazy rescale
+        // online softmax (base 2), lazy rescale; the IEEE maximum (v_maximum3_f32) needs
+        // no input canonicalisation, unlike fmaxf on MFMA results
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s[kb][r], s[kb][r + 1]));
+            for (int r = 0; r < 16; r += 2)
+                mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(s[kb][r], s[kb][r + 1]));
         if (__ballot(mx * a.c > m2 + RESCALE_SLACK) != 0ull) {
             mx = fmaxf(mx, swap_halves(mx));
             const float mnew = fmaxf(m2, mx * a.c);
@@ -399,7 +406,8 @@ __global__ __launch_bounds__(512) void fwd_dense_kernel(FwdArgs a) {
             for (int db = 0; db < 4; ++db)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-            lsum *= alpha;
+            lsum[0] *= alpha;
+            lsum[1] *= alpha;
             m2 = mnew;
         }
         const float msub = (m2 == -INFINITY) ? 0.f : m2;
@@ -412,7 +420,7 @@ __global__ __launch_bounds__(512) void fwd_dense_kernel(FwdArgs a) {
             for (int e2 = 0; e2 < 8; e2 += 2) {
                 const float p0 = fast_exp2(fmaf(s[kk >> 1][(kk & 1) * 8 + e2], a.c, -msub));
                 const float p1 = fast_exp2(fmaf(s[kk >> 1][(kk & 1) * 8 + e2 + 1], a.c, -msub));
-                lsum += p0 + p1;
+                lsum[kk & 1] += p0 + p1;
                 pk[e2 >> 1] = pack_bf16(p0, p1);
             }
             pb[kk] = as_bf16x8(pk);
@@ -434,7 +442,8 @@ __global__ __launch_bounds__(512) void fwd_dense_kernel(FwdArgs a) {
         lds_barrier();
     }
 
-    const float ltot = lsum + swap_halves(lsum);
+    const float lrow = lsum[0] + lsum[1];
+    const float ltot = lrow + swap_halves(lrow);
     if (row_ok) {
         const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
         bf16* op = a.o + ((size_t)pos * a.Hq + head) * HEAD_DIM;
