@@ -552,6 +552,7 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) _Float16 Kh[2][FWD_BN * HEAD_DIM];   // swizzled rows
     __shared__ __attribute__((aligned(16))) _Float16 Vh[2][FWD_BN * HEAD_DIM];   // swizzled rows
     __shared__ int4 Ds[2][FWD_BN];
+    __shared__ __attribute__((aligned(16))) uint32_t Mb[NW][FWD_BN];   // per wave: key -> position bits
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int l32 = lane & 31, hf = lane >> 5;
@@ -564,11 +565,13 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
     const float inv_sV = 1.f / sV;
 
     int head, pos, lb, le;
+    int p_base = 0;   // the wave's rows cover positions p_base + (0 .. 31) (dense masks)
     if constexpr (!SPARSE) {
         const int qt = a.order[y];
         const int R = w * 32 + l32;
         head = g * a.G + (R >> a.lgBMq);
         pos = qt * a.BMq + (R & (a.BMq - 1));
+        p_base = qt * a.BMq + ((w * 32) & (a.BMq - 1));
         lb = a.ptr[qt];
         le = a.ptr[qt + 1];
     } else {
@@ -670,6 +673,12 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
         const bool need_mask = t + 1 < ntiles ? mask_cur : mask_nxt;
         const _Float16* kt = Kh[cb];
         const _Float16* vt = Vh[cb];
+        if (!SPARSE && need_mask) {
+            // lane j: key j's two row intervals as a bit mask over the wave's positions
+            const int4 d = Ds[cb][lane];
+            Mb[w][lane] = interval_bits(d.x, d.y, p_base) | interval_bits(d.z, d.w, p_base);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's masks written
+        }
         // per 32-key half kb: S^T = K Q^T and dP^T = V dO^T (lane column = its query row,
         // rows = keys), dS^T, then dQ^T += (K * sK)^T (dS^T * sO) for those 32 keys
 #pragma unroll
@@ -707,9 +716,7 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
                             if constexpr (SPARSE) {
                                 vis = key0 + kidx < T;
                             } else {
-                                const int4 d = Ds[cb][kidx];
-                                vis = ((unsigned)(pos - d.x) < (unsigned)(d.y - d.x)) |
-                                      ((unsigned)(pos - d.z) < (unsigned)(d.w - d.z));
+                                vis = (int)(Mb[w][kidx] << (31 - (pos - p_base))) < 0;
                             }
                         }
                         const float p = vis ? fast_exp2(fmaf(st[r], cS, -lse2)) : 0.f;

@@ -72,6 +72,14 @@ __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// Bits b = 0..31 with base + b in [lo, hi): the rows of a half-open row interval among 32
+// consecutive positions starting at base.
+__device__ __forceinline__ uint32_t interval_bits(int lo, int hi, int base) {
+    const int a = min(max(lo - base, 0), 32), b = min(max(hi - base, 0), 32);
+    const uint64_t m = ((1ull << b) - 1ull) & ~((1ull << a) - 1ull);
+    return (uint32_t)m;
+}
+
 // Exchange a float with the lane 32 positions away (the other half of the wave).
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32); }
 

@@ -279,6 +279,7 @@ __global__ __launch_bounds__(512) void fwd_dense_kernel(FwdArgs a) {
     __shared__ __attribute__((aligned(16))) bf16 Kb[2][FWD_BN * K_LD];
     __shared__ __attribute__((aligned(16))) bf16 Vb[2][FWD_BN * V_LD];
     __shared__ int4 Db[2][FWD_BN];
+    __shared__ __attribute__((aligned(16))) uint32_t Mb[8][FWD_BN];   // per wave: key -> position bits
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int l32 = lane & 31, hf = lane >> 5;
@@ -292,6 +293,10 @@ __global__ __launch_bounds__(512) void fwd_dense_kernel(FwdArgs a) {
     const int lb = a.ptr[qt], le = a.ptr[qt + 1];
     const bool row_ok = pos < T;
     const int n = le - lb;
+    // the wave's rows cover positions p_base + (0 .. 31) (fewer when a query tile has under
+    // 32 positions); this row's bit in a per-key position mask is pos - p_base
+    const int p_base = qt * a.BMq + ((w * 32) & (a.BMq - 1));
+    const int bit_shift = 31 - (pos - p_base);
 
     f32x16 acc[4];
 #pragma unroll
@@ -378,15 +383,22 @@ __global__ __launch_bounds__(512) void fwd_dense_kernel(FwdArgs a) {
             [&](int i, u32x4 op) { s[i & 1] = mfma32(as_bf16x8(op), qf[i >> 1], s[i & 1]); });
 
         if (need_mask) {
-            const int4* dbuf = Db[cb];
+            // Lane j turns key j's two row intervals into a bit mask over the wave's (at
+            // most 32) distinct positions p_base .. p_base + 31; every lane then tests its
+            // own position's bit in the masks of the 32 keys it holds.
+            const int4 d = Db[cb][lane];
+            Mb[w][lane] = interval_bits(d.x, d.y, p_base) | interval_bits(d.z, d.w, p_base);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's masks written
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int4 d = dbuf[kb * 32 + acc_row(r, hf)];
-                    const bool vis = ((unsigned)(pos - d.x) < (unsigned)(d.y - d.x)) |
-                                     ((unsigned)(pos - d.z) < (unsigned)(d.w - d.z));
-                    s[kb][r] = vis ? s[kb][r] : -INFINITY;
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const u32x4 m4 = *reinterpret_cast<const u32x4*>(&Mb[w][kb * 32 + 8 * q4 + 4 * hf]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const bool vis = (int)(m4[i] << bit_shift) < 0;
+                        s[kb][4 * q4 + i] = vis ? s[kb][4 * q4 + i] : -INFINITY;
+                    }
                 }
         }
 

@@ -83,6 +83,12 @@ def test_gqa16_rows_span_heads():
     _check(333, 16, 1, MaskSpec("causal"), seed=8)
 
 
+def test_gqa32_document_rows_span_heads():
+    # G = 32: a 32-row block holds four heads x 8 positions; PARTIAL tiles everywhere
+    T = 300
+    _check(T, 32, 1, MaskSpec("causal_document", cu_seqlens=document_cu_seqlens(14, T, 20, 90)), seed=14)
+
+
 def test_single_position():
     _check(1, 8, 2, MaskSpec("causal"), seed=9)
 
