@@ -376,12 +376,23 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
         if (!full && key_ok) {
             const RowMap rm = row_map<SPARSE>(a, g, e);
             const int rb = st & (RB - 1);
-            vis = 0u;
+            if (rm.mask >= 31) {
+                // the step's 32 rows are 32 consecutive positions from p0: this key's two
+                // row intervals as a bit mask over them, then the lane's 16 rows
+                // (bits 8q + 4hf + i, q, i < 4) packed into bits 4q + i
+                const int p0 = rm.pbase + ((rb * 32) & rm.mask);
+                uint32_t m = (interval_bits(kd.x, kd.y, p0) | interval_bits(kd.z, kd.w, p0)) >> (4 * hf);
+                m &= 0x0F0F0F0Fu;
+                m = (m | (m >> 4)) & 0x00FF00FFu;
+                vis = (m | (m >> 8)) & 0xFFFFu;
+            } else {
+                vis = 0u;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int p = rm.pos(rb * 32 + acc_row(r, hf));
-                const bool v = (p >= kd.x && p < kd.y) || (p >= kd.z && p < kd.w);
-                vis |= (uint32_t)v << r;
+                for (int r = 0; r < 16; ++r) {
+                    const int p = rm.pos(rb * 32 + acc_row(r, hf));
+                    const bool v = (p >= kd.x && p < kd.y) || (p >= kd.z && p < kd.w);
+                    vis |= (uint32_t)v << r;
+                }
             }
         }
         _Float16* ps = Ps[st & 1];
