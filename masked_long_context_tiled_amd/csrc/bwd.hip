@@ -108,35 +108,42 @@ __global__ void zero_stats_kernel(float* __restrict__ stats) {
 }
 
 // D[h][i] = sum_c dO[i][h][c] * (O + O_lo)[i][h][c], and max_i ||dO_i||^2.
-// 16 lanes per (position, head) row.
+// 16 lanes per (position, head) row; a grid-stride loop over groups of 16 rows, so the
+// per-workgroup maximum reaches the single bound slot with few atomics. The loop bound is
+// uniform over the workgroup, so every lane reaches the shuffles.
 __global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* __restrict__ o, const bf16* __restrict__ o_lo,
                                                       const bf16* __restrict__ dout, float* __restrict__ dbuf,
                                                       float* __restrict__ stats, int T, int Hq) {
-    const long row = (long)blockIdx.x * 16 + (threadIdx.x >> 4);
+    const long nrows = (long)T * Hq;
     const int part = threadIdx.x & 15;
-    float s = 0.f, n2 = 0.f;
-    if (row < (long)T * Hq) {
-        const u32x4 x = *reinterpret_cast<const u32x4*>(o + row * HEAD_DIM + part * 8);
-        const u32x4 y = *reinterpret_cast<const u32x4*>(dout + row * HEAD_DIM + part * 8);
-        u32x4 z = {0u, 0u, 0u, 0u};
-        if (o_lo) z = *reinterpret_cast<const u32x4*>(o_lo + row * HEAD_DIM + part * 8);
+    float best = 0.f;
+    for (long base = (long)blockIdx.x * 16; base < nrows; base += (long)gridDim.x * 16) {
+        const long row = base + (threadIdx.x >> 4);
+        float s = 0.f, n2 = 0.f;
+        if (row < nrows) {
+            const u32x4 x = *reinterpret_cast<const u32x4*>(o + row * HEAD_DIM + part * 8);
+            const u32x4 y = *reinterpret_cast<const u32x4*>(dout + row * HEAD_DIM + part * 8);
+            u32x4 z = {0u, 0u, 0u, 0u};
+            if (o_lo) z = *reinterpret_cast<const u32x4*>(o_lo + row * HEAD_DIM + part * 8);
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const float d0 = bf16_lo(y[m]), d1 = bf16_hi(y[m]);
-            s += d0 * (bf16_lo(x[m]) + bf16_lo(z[m])) + d1 * (bf16_hi(x[m]) + bf16_hi(z[m]));
-            n2 += d0 * d0 + d1 * d1;
+            for (int m = 0; m < 4; ++m) {
+                const float d0 = bf16_lo(y[m]), d1 = bf16_hi(y[m]);
+                s += d0 * (bf16_lo(x[m]) + bf16_lo(z[m])) + d1 * (bf16_hi(x[m]) + bf16_hi(z[m]));
+                n2 += d0 * d0 + d1 * d1;
+            }
         }
-    }
 #pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) {
-        s += __shfl_xor(s, off);
-        n2 += __shfl_xor(n2, off);
+        for (int off = 8; off >= 1; off >>= 1) {
+            s += __shfl_xor(s, off);
+            n2 += __shfl_xor(n2, off);
+        }
+        if (part == 0 && row < nrows) {
+            const int pos = (int)(row / Hq), head = (int)(row % Hq);
+            dbuf[(size_t)head * T + pos] = s;
+        }
+        best = fmaxf(best, n2);
     }
-    if (part == 0 && row < (long)T * Hq) {
-        const int pos = (int)(row / Hq), head = (int)(row % Hq);
-        dbuf[(size_t)head * T + pos] = s;
-    }
-    block_max_to(stats + ST_DO_NORM2, n2);
+    block_max_to(stats + ST_DO_NORM2, best);
 }
 
 // max |x| over n8 chunks of 8 bf16.
@@ -773,7 +780,8 @@ hipError_t launch_bwd_pre(const Problem& P, const void* q, const void* k, const 
     float* stats = reinterpret_cast<float*>(ws + W.stats);
     hipLaunchKernelGGL(zero_stats_kernel, dim3(1), dim3(64), 0, s, stats);
     const long rows = (long)P.T * P.Hq;
-    hipLaunchKernelGGL(bwd_pre_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s,
+    const long groups = (rows + 15) / 16;
+    hipLaunchKernelGGL(bwd_pre_kernel, dim3((unsigned)(groups < 4096 ? groups : 4096)), dim3(256), 0, s,
                        static_cast<const bf16*>(o), static_cast<const bf16*>(o_lo), static_cast<const bf16*>(dout),
                        dbuf, stats, P.T, P.Hq);
     const size_t nq8 = (size_t)P.T * P.Hq * HEAD_DIM / 8, nk8 = (size_t)P.T * P.Hk * HEAD_DIM / 8;
