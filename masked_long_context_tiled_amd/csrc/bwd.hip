@@ -719,31 +719,35 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
             // dS^T * sO = P^T * (dP^T * sO - D * sO), as B operands of two 16-key steps;
             // key slot (hf, e) of step kk is key kb*32 + 16*kk + 8*(e/4) + 4*hf + e%4
             f16x8 sb[2];
+            // two copies of the element loop, so that a FULL tile carries no mask test
+            auto form_ds = [&](auto masked_tag) {
+                constexpr bool masked = decltype(masked_tag)::value;
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                u32x4 pk;
+                for (int kk = 0; kk < 2; ++kk) {
+                    u32x4 pk;
 #pragma unroll
-                for (int e2 = 0; e2 < 8; e2 += 2) {
-                    float v2[2];
+                    for (int e2 = 0; e2 < 8; e2 += 2) {
+                        float v2[2];
 #pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const int r = kk * 8 + e2 + j;
-                        const int kidx = kb * 32 + acc_row(r, hf);
-                        bool vis = true;
-                        if (need_mask) {
-                            if constexpr (SPARSE) {
-                                vis = key0 + kidx < T;
-                            } else {
-                                vis = (int)(Mb[w][kidx] << (31 - (pos - p_base))) < 0;
+                        for (int j = 0; j < 2; ++j) {
+                            const int r = kk * 8 + e2 + j;
+                            const int kidx = kb * 32 + acc_row(r, hf);
+                            float p = fast_exp2(fmaf(st[r], cS, -lse2));
+                            if constexpr (masked) {
+                                bool vis;
+                                if constexpr (SPARSE) vis = key0 + kidx < T;
+                                else vis = (int)(Mb[w][kidx] << (31 - (pos - p_base))) < 0;
+                                p = vis ? p : 0.f;
                             }
+                            v2[j] = p * fmaf(dpt[r], inv_sV, -dd);
                         }
-                        const float p = vis ? fast_exp2(fmaf(st[r], cS, -lse2)) : 0.f;
-                        v2[j] = p * fmaf(dpt[r], inv_sV, -dd);
+                        pk[e2 >> 1] = pack_f16(v2[0], v2[1]);
                     }
-                    pk[e2 >> 1] = pack_f16(v2[0], v2[1]);
+                    sb[kk] = as_f16x8(pk);
                 }
-                sb[kk] = as_f16x8(pk);
-            }
+            };
+            if (need_mask) form_ds(BoolTag<true>{});
+            else form_ds(BoolTag<false>{});
             mfma_pipelined<8>(
                 [&](int i) {
                     const int k0 = kb * 32 + 16 * (i & 1) + 4 * hf;

@@ -72,6 +72,12 @@ __device__ __forceinline__ uint32_t pack_f16(float lo, float hi) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// Compile-time flag passed to generic lambdas (decltype(tag)::value).
+template <bool B>
+struct BoolTag {
+    static constexpr bool value = B;
+};
+
 // Bits b = 0..31 with base + b in [lo, hi): the rows of a half-open row interval among 32
 // consecutive positions starting at base.
 __device__ __forceinline__ uint32_t interval_bits(int lo, int hi, int base) {
