@@ -24,8 +24,6 @@
 
 namespace mlct {
 
-constexpr int KS_LD = HEAD_DIM + 8;   // bf16 per K row in LDS (pad against bank conflicts)
-constexpr int VT_LD = FWD_BN + 4;     // bf16 per V^T row in LDS
 constexpr float RESCALE_SLACK = 8.0f; // log2 units the running max may lag behind
 
 struct FwdArgs {
@@ -43,18 +41,35 @@ struct FwdArgs {
     float c;   // scale * log2(e)
 };
 
+// LDS row strides: K's 16-byte row reads and V's transposed reads (V is staged row-major
+// and V^T read with ds_read_b64_tr_b16, no transposing stores) are free of bank conflicts
+// at 136 and 144 bf16. Every MFMA's LDS operand is read three MFMAs ahead.
+constexpr int K_LD = HEAD_DIM + 8;    // bf16 per K row in LDS
+constexpr int V_LD = HEAD_DIM + 16;   // bf16 per V row in LDS
+
+// A operand (32 rows x 16 k) of 16-bit elements whose row m = lane % 32 is column c0 + m
+// of the row-major [rows][ld] matrix M; k-slots e = 0..3 are rows r_lo + e, e = 4..7 rows
+// r_hi + e - 4 (callers fold the lane half into r_lo / r_hi).
+__device__ __forceinline__ u32x4 tr_rows_ld(const bf16* M, int ld, int r_lo, int r_hi, int c0, int lane) {
+    const int s = lane & 15;
+    const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (s & 3);
+    const u32x2 lo = ds_read_tr16(M + (r_lo + (s >> 2)) * ld + col);
+    const u32x2 hi = ds_read_tr16(M + (r_hi + (s >> 2)) * ld + col);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
 // Block-sparse work items: one (query head, query block) row of the keep matrix, b/32
-// waves, each list entry a b-key block walked as b/64 tiles. K is staged in padded rows,
-// V transposed, single-buffered with two barriers per tile.
+// waves, each list entry a b-key block walked as b/64 tiles. K and V are staged row-major
+// (V^T read with transposed LDS reads, as in the dense kernel), single-buffered with two
+// barriers per tile (the small LDS footprint keeps four work items per CU).
 template <int NW>
 __global__ __launch_bounds__(NW * 64) void fwd_sparse_kernel(FwdArgs a) {
     constexpr int NT = NW * 64;
-    constexpr int KCH = 1024 / NT;   // 16-byte K chunks per thread per tile
-    constexpr int VUN = 512 / NT;    // (key pair, 8 dims) V units per thread per tile
-    constexpr int TPE = NW / 2;   // 64-key tiles per list entry
+    constexpr int CPT = 1024 / NT;   // 16-byte chunks per thread per tile per tensor
+    constexpr int TPE = NW / 2;      // 64-key tiles per list entry
 
-    __shared__ __attribute__((aligned(16))) bf16 Ks[FWD_BN * KS_LD];
-    __shared__ __attribute__((aligned(16))) bf16 Vt[HEAD_DIM * VT_LD];
+    __shared__ __attribute__((aligned(16))) bf16 Ks[FWD_BN * K_LD];
+    __shared__ __attribute__((aligned(16))) bf16 Vs[FWD_BN * V_LD];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int l32 = lane & 31, hf = lane >> 5;
@@ -70,16 +85,16 @@ __global__ __launch_bounds__(NW * 64) void fwd_sparse_kernel(FwdArgs a) {
     const bool row_ok = pos < T;
     const int ntiles = (le - lb) * TPE;
 
-    // Q row fragments: B operand, lane holds dims 16*ks + 8*hf .. +7 of its row.
+    // Q row fragments: B operand, lane holds dims 16*ks + 8*hf .. +7 of its row; the loads
+    // complete before the loop (left pending, the first wait in the loop would also cover
+    // the K/V loads issued behind them)
     bf16x8 qf[8];
     {
-        const bf16* qp = a.q + ((size_t)pos * a.Hq + head) * HEAD_DIM + 8 * hf;
+        const bf16* qp = a.q + ((size_t)min(pos, T - 1) * a.Hq + head) * HEAD_DIM + 8 * hf;
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            u32x4 x = {0u, 0u, 0u, 0u};
-            if (row_ok) x = *reinterpret_cast<const u32x4*>(qp + 16 * ks);
-            qf[ks] = as_bf16x8(x);
-        }
+        for (int ks = 0; ks < 8; ++ks) qf[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qp + 16 * ks));
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) asm volatile("" ::"v"(as_u32x4(qf[ks])));
     }
 
     f32x16 acc[4];
@@ -87,76 +102,54 @@ __global__ __launch_bounds__(NW * 64) void fwd_sparse_kernel(FwdArgs a) {
     for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
-    float m2 = -INFINITY, lsum = 0.f;
+    float m2 = -INFINITY, lsum[2] = {0.f, 0.f};
 
     const bf16* kbase = a.k + (size_t)g * HEAD_DIM;
     const bf16* vbase = a.v + (size_t)g * HEAD_DIM;
     const size_t kv_row = (size_t)a.Hk * HEAD_DIM;
 
-    u32x4 kreg[KCH], v0reg[VUN], v1reg[VUN];
+    // Rows past the end are read from row T - 1 (finite data; such keys are masked).
+    u32x4 kreg[CPT], vreg[CPT];
     int nkey0 = 0;
-    bool nmask = false;
+    auto load_tile = [&](int t) {
+        const int e = a.ent[lb + t / TPE];
+        nkey0 = e * a.sblock + (t % TPE) * FWD_BN;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+            const int c = tid + i * NT, key = min(nkey0 + (c >> 4), T - 1);
+            const size_t o = (size_t)key * kv_row + (c & 15) * 8;
+            kreg[i] = *reinterpret_cast<const u32x4*>(kbase + o);
+            vreg[i] = *reinterpret_cast<const u32x4*>(vbase + o);
+        }
+    };
 
-    // Issue the global loads of tile t into registers.
-#define FWD_LOAD_TILE(t)                                                                       \
-    {                                                                                          \
-        const int e_ = a.ent[lb + (t) / TPE];                                                  \
-        nkey0 = e_ * a.sblock + ((t) % TPE) * FWD_BN;                                          \
-        nmask = nkey0 + FWD_BN > T;                                                            \
-        _Pragma("unroll") for (int i = 0; i < KCH; ++i) {                                      \
-            const int c_ = tid + i * NT, key_ = nkey0 + (c_ >> 4);                             \
-            u32x4 x_ = {0u, 0u, 0u, 0u};                                                       \
-            if (key_ < T) x_ = *reinterpret_cast<const u32x4*>(kbase + key_ * kv_row + (c_ & 15) * 8); \
-            kreg[i] = x_;                                                                      \
-        }                                                                                      \
-        _Pragma("unroll") for (int i = 0; i < VUN; ++i) {                                      \
-            const int u_ = tid + i * NT, key_ = nkey0 + 2 * (u_ & 31), d0_ = (u_ >> 5) * 8;    \
-            u32x4 x0_ = {0u, 0u, 0u, 0u}, x1_ = {0u, 0u, 0u, 0u};                              \
-            if (key_ < T) x0_ = *reinterpret_cast<const u32x4*>(vbase + key_ * kv_row + d0_);  \
-            if (key_ + 1 < T) x1_ = *reinterpret_cast<const u32x4*>(vbase + (key_ + 1) * kv_row + d0_); \
-            v0reg[i] = x0_;                                                                    \
-            v1reg[i] = x1_;                                                                    \
-        }                                                                                      \
-    }
-
-    if (ntiles > 0) FWD_LOAD_TILE(0);
+    if (ntiles > 0) load_tile(0);
 
     for (int t = 0; t < ntiles; ++t) {
         const int key0 = nkey0;
-        const bool need_mask = nmask;
+        const bool need_mask = key0 + FWD_BN > T;
 
         __syncthreads();   // every wave is done reading the previous tile
 #pragma unroll
-        for (int i = 0; i < KCH; ++i) {
-            const int c = tid + i * NT;
-            *reinterpret_cast<u32x4*>(&Ks[(c >> 4) * KS_LD + (c & 15) * 8]) = kreg[i];
+        for (int i = 0; i < CPT; ++i) {
+            const int c = tid + i * NT, row = c >> 4, col = (c & 15) * 8;
+            *reinterpret_cast<u32x4*>(&Ks[row * K_LD + col]) = kreg[i];
+            *reinterpret_cast<u32x4*>(&Vs[row * V_LD + col]) = vreg[i];
         }
-#pragma unroll
-        for (int i = 0; i < VUN; ++i) {
-            const int u = tid + i * NT, p = u & 31, d0 = (u >> 5) * 8;
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const uint32_t x0 = v0reg[i][m], x1 = v1reg[i][m];
-                // (V[2p][d], V[2p+1][d]) for d = d0 + 2m and d0 + 2m + 1
-                *reinterpret_cast<uint32_t*>(&Vt[(d0 + 2 * m) * VT_LD + 2 * p]) = (x0 & 0xffffu) | (x1 << 16);
-                *reinterpret_cast<uint32_t*>(&Vt[(d0 + 2 * m + 1) * VT_LD + 2 * p]) = (x0 >> 16) | (x1 & 0xffff0000u);
-            }
-        }
-        __syncthreads();
+        lds_barrier();
 
-        if (t + 1 < ntiles) FWD_LOAD_TILE(t + 1);
+        if (t + 1 < ntiles) load_tile(t + 1);
 
-        // S^T = K Q^T for the two 32-key halves of the tile.
+        // S^T = K Q^T for the two 32-key halves of the tile
         f32x16 s[2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-            const bf16* kr = Ks + (kb * 32 + l32) * KS_LD + 8 * hf;
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks)
-                s[kb] = mfma32(*reinterpret_cast<const bf16x8*>(kr + 16 * ks), qf[ks], s[kb]);
-        }
+        const bf16* kr = Ks + l32 * K_LD + 8 * hf;
+        mfma_pipelined<16>(
+            [&](int i) { return *reinterpret_cast<const u32x4*>(kr + (i & 1) * 32 * K_LD + 16 * (i >> 1)); },
+            [&](int i, u32x4 op) { s[i & 1] = mfma32(as_bf16x8(op), qf[i >> 1], s[i & 1]); });
 
         if (need_mask) {
 #pragma unroll
@@ -168,22 +161,23 @@ __global__ __launch_bounds__(NW * 64) void fwd_sparse_kernel(FwdArgs a) {
                 }
         }
 
-        // online softmax (base 2)
+        // online softmax (base 2), lazy rescale
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-        mx = fmaxf(mx, swap_halves(mx));
-        const float cand = mx * a.c;
-        if (__ballot(cand > m2 + RESCALE_SLACK) != 0ull) {
-            const float mnew = fmaxf(m2, cand);
+            for (int r = 0; r < 16; r += 2)
+                mx = __builtin_elementwise_maximum(mx, __builtin_elementwise_maximum(s[kb][r], s[kb][r + 1]));
+        if (__ballot(mx * a.c > m2 + RESCALE_SLACK) != 0ull) {
+            mx = fmaxf(mx, swap_halves(mx));
+            const float mnew = fmaxf(m2, mx * a.c);
             const float alpha = (m2 == -INFINITY) ? 0.f : fast_exp2(m2 - mnew);
 #pragma unroll
             for (int db = 0; db < 4; ++db)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-            lsum *= alpha;
+            lsum[0] *= alpha;
+            lsum[1] *= alpha;
             m2 = mnew;
         }
         const float msub = (m2 == -INFINITY) ? 0.f : m2;
@@ -193,31 +187,26 @@ __global__ __launch_bounds__(NW * 64) void fwd_sparse_kernel(FwdArgs a) {
         for (int kk = 0; kk < 4; ++kk) {
             u32x4 pk;
 #pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-                const float p0 = fast_exp2(fmaf(s[kk >> 1][(kk & 1) * 8 + e], a.c, -msub));
-                const float p1 = fast_exp2(fmaf(s[kk >> 1][(kk & 1) * 8 + e + 1], a.c, -msub));
-                lsum += p0 + p1;
-                pk[e >> 1] = pack_bf16(p0, p1);
+            for (int e2 = 0; e2 < 8; e2 += 2) {
+                const float p0 = fast_exp2(fmaf(s[kk >> 1][(kk & 1) * 8 + e2], a.c, -msub));
+                const float p1 = fast_exp2(fmaf(s[kk >> 1][(kk & 1) * 8 + e2 + 1], a.c, -msub));
+                lsum[kk & 1] += p0 + p1;
+                pk[e2 >> 1] = pack_bf16(p0, p1);
             }
             pb[kk] = as_bf16x8(pk);
         }
 
         // O^T += V^T P^T: key slot (hf, e) of step kk is key 16*kk + 8*(e/4) + 4*hf + e%4.
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-            const bf16* vr = Vt + (db * 32 + l32) * VT_LD + 4 * hf;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const u32x2 lo = *reinterpret_cast<const u32x2*>(vr + 16 * kk);
-                const u32x2 hi = *reinterpret_cast<const u32x2*>(vr + 16 * kk + 8);
-                const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
-                acc[db] = mfma32(as_bf16x8(av), pb[kk], acc[db]);
-            }
-        }
+        mfma_pipelined<16>(
+            [&](int i) {
+                const int kk = i >> 2, db = i & 3;
+                return tr_rows_ld(Vs, V_LD, 16 * kk + 4 * hf, 16 * kk + 8 + 4 * hf, db * 32, lane);
+            },
+            [&](int i, u32x4 op) { acc[i & 3] = mfma32(as_bf16x8(op), pb[i >> 2], acc[i & 3]); });
     }
-#undef FWD_LOAD_TILE
 
-    const float ltot = lsum + swap_halves(lsum);
+    const float lrow = lsum[0] + lsum[1];
+    const float ltot = lrow + swap_halves(lrow);
     if (row_ok) {
         const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
         bf16* op = a.o + ((size_t)pos * a.Hq + head) * HEAD_DIM;
@@ -246,32 +235,15 @@ __global__ __launch_bounds__(NW * 64) void fwd_sparse_kernel(FwdArgs a) {
 }
 
 // Dense work items (the G heads of one KV head x 256/G positions, 8 waves of 32 rows).
-// Same arithmetic as fwd_sparse_kernel, organised for fewer stalls:
+// Same arithmetic as fwd_sparse_kernel, with these differences:
 //  - K, V and the column descriptors are double-buffered in LDS: while tile t is
 //    computed from slot t % 2, tile t + 1 (loaded one tile earlier) is stored into the
 //    other slot and the loads of tile t + 2 are issued; one barrier per tile;
-//  - V is kept row-major and V^T is read with transposed LDS reads (no transposing
-//    stores); the row strides (136 and 144 bf16) make both K's row reads and V's
-//    transposed reads free of bank conflicts;
-//  - every MFMA's LDS operand is read three MFMAs ahead;
+//  - PARTIAL tiles are masked through per-key bit masks over the wave's positions;
 //  - list entries are read from registers filled a chunk ahead, so no load waits on a
 //    freshly loaded entry;
 //  - the in-lane row max covers half of a row's keys; the two halves are combined only
 //    when the running max has to move (the lazy rescale).
-constexpr int K_LD = HEAD_DIM + 8;    // bf16 per K row in LDS
-constexpr int V_LD = HEAD_DIM + 16;   // bf16 per V row in LDS
-
-// A operand (32 rows x 16 k) of 16-bit elements whose row m = lane % 32 is column c0 + m
-// of the row-major [rows][ld] matrix M; k-slots e = 0..3 are rows r_lo + e, e = 4..7 rows
-// r_hi + e - 4 (callers fold the lane half into r_lo / r_hi).
-__device__ __forceinline__ u32x4 tr_rows_ld(const bf16* M, int ld, int r_lo, int r_hi, int c0, int lane) {
-    const int s = lane & 15;
-    const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (s & 3);
-    const u32x2 lo = ds_read_tr16(M + (r_lo + (s >> 2)) * ld + col);
-    const u32x2 hi = ds_read_tr16(M + (r_hi + (s >> 2)) * ld + col);
-    return u32x4{lo[0], lo[1], hi[0], hi[1]};
-}
-
 __global__ __launch_bounds__(512) void fwd_dense_kernel(FwdArgs a) {
     constexpr int NT = 512;
     constexpr int CPT = 1024 / NT;   // 16-byte chunks per thread per tile per tensor
