@@ -267,7 +267,9 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) float lse_s[3][32];
     __shared__ __attribute__((aligned(16))) float dd_s[2][32];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // wave index made uniform (SGPR), so the role branches are scalar branches
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l32 = lane & 31, hf = lane >> 5;
     const bool is_a = w < NWK;
     const int kb = is_a ? w : w - NWK;
