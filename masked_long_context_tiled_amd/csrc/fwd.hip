@@ -108,11 +108,16 @@ __global__ __launch_bounds__(NW * 64) void fwd_sparse_kernel(FwdArgs a) {
     const bf16* vbase = a.v + (size_t)g * HEAD_DIM;
     const size_t kv_row = (size_t)a.Hk * HEAD_DIM;
 
+    // list entries from registers filled a chunk of 64 ahead (no tile waits on a freshly
+    // loaded entry before it can address its K/V loads)
+    EntryStream es;
+    es.init(a.ent, lb, le - lb, lane);
+
     // Rows past the end are read from row T - 1 (finite data; such keys are masked).
     u32x4 kreg[CPT], vreg[CPT];
     int nkey0 = 0;
     auto load_tile = [&](int t) {
-        const int e = a.ent[lb + t / TPE];
+        const int e = es.get(t / TPE, lane);
         nkey0 = e * a.sblock + (t % TPE) * FWD_BN;
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
