@@ -94,3 +94,37 @@ def test_lse_merge_empty_partial_keeps_accumulator():
                    torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     assert torch.equal(o, o0) and torch.equal(lse, lse0)
+
+
+@pytest.mark.parametrize("G", [4, 16])
+def test_chunk_pair_with_fully_masked_rows(G):
+    """One CAUSAL chunk pair whose key chunk starts after some of its queries: those rows
+    see no key (O = 0, LSE = -inf, zero gradients), the rest see a ragged causal block; the
+    backward uses the pair's own O and LSE. Checked against the fp64 chunk oracle."""
+    import torch
+    from oracle.chunks import chunk_backward, chunk_forward
+    T, n, q0, k0, Hk = 1300, 500, 100, 390, 1
+    Hq = G * Hk
+    spec = MaskSpec("causal")
+    note(f"chunk pair with empty rows G={G} T={T} n={n} q0={q0} k0={k0}")
+    x = attention_inputs(60 + G, T, Hq, Hk)
+    xo = oracle_inputs(x)
+    qs, ks = slice(q0, q0 + n), slice(k0, k0 + n)
+    q, k, v, do = (to_dev_bf16(np.ascontiguousarray(x[m][sl]), torch)
+                   for m, sl in (("q", qs), ("k", ks), ("v", ks), ("do", qs)))
+    ma = attn.MaskedAttention(n, Hq, Hk, spec, desc=attn.mask_desc_build_chunk(spec, T, q0, k0, n))
+    o, lse, o_lo = ma.forward(q, k, v)
+    dq, dk, dv = ma.backward(q, k, v, o, lse, do, o_lo=o_lo)
+    torch.cuda.synchronize()
+    ro, rl = chunk_forward(xo["q"][qs], xo["k"][ks], xo["v"][ks], spec, T, q0, k0)
+    rdq, rdk, rdv = chunk_backward(xo["q"][qs], xo["k"][ks], xo["v"][ks], xo["do"][qs], ro, rl, spec, T, q0, k0)
+    lse_h = lse.cpu().numpy()
+    empty = np.isneginf(rl)
+    assert empty.any() and not empty.all()
+    assert np.array_equal(np.isneginf(lse_h), empty)
+    errs = [assert_close("O", bf16_dev_to_f64(o), ro, TOL), assert_close("LSE", lse_h, rl, LSE_TOL),
+            assert_close("dQ", dq.cpu().numpy(), rdq, TOL), assert_close("dK", dk.cpu().numpy(), rdk, TOL),
+            assert_close("dV", dv.cpu().numpy(), rdv, TOL)]
+    rows = np.nonzero(empty[0])[0]
+    assert (bf16_dev_to_f64(o)[rows] == 0).all() and (dq.cpu().numpy()[rows] == 0).all()
+    note("  max errors " + " ".join(f"{e:.2e}" for e in errs))
