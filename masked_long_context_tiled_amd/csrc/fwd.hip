@@ -14,11 +14,12 @@
 // feed O^T += V^T P^T directly as the B operand (no register shuffles); the A operand
 // V^T comes from LDS.
 //
-// Per tile: EMPTY tiles are not in the list; FULL tiles skip all mask work; PARTIAL
-// tiles (and the ragged last tile) test each element against the key's two visible row
-// intervals. Online softmax runs in base 2 with a lazy rescale: the running max used
-// for the exponent is only raised when a row's new max exceeds it by more than 8
-// (so P <= 2^8), which keeps the O rescale off the common path; O / l and
+// Per tile: EMPTY tiles are not in the list; FULL tiles skip all mask work; on PARTIAL
+// tiles (and the ragged last tile) each key's two visible row intervals become one bit
+// mask over the wave's positions, which every lane tests for its own row (block-sparse
+// tiles only mask keys past the end). Online softmax runs in base 2 with a lazy rescale:
+// the running max used for the exponent is only raised when a row's new max exceeds it by
+// more than 8 (so P <= 2^8), which keeps the O rescale off the common path; O / l and
 // LSE = (m + log2 l) * ln 2 are exact whatever max was used.
 #include "common.h"
 
