@@ -569,8 +569,11 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
     constexpr int CPT = 1024 / NT;               // 16-byte chunks per thread per tile per tensor
     constexpr int TPE = SPARSE ? NW / 2 : 1;     // 64-key tiles per list entry
 
-    __shared__ __attribute__((aligned(16))) _Float16 Kh[2][FWD_BN * HEAD_DIM];   // swizzled rows
-    __shared__ __attribute__((aligned(16))) _Float16 Vh[2][FWD_BN * HEAD_DIM];   // swizzled rows
+    // Padded rows (fp16 per row): K is read as rows (S^T) and transposed (dQ^T), V as rows
+    // only; these strides measured faster than the XOR swizzle of the staged backward rows.
+    constexpr int KLD = HEAD_DIM + 16, VLD = HEAD_DIM + 8;
+    __shared__ __attribute__((aligned(16))) _Float16 Kh[2][FWD_BN * KLD];
+    __shared__ __attribute__((aligned(16))) _Float16 Vh[2][FWD_BN * VLD];
     __shared__ int4 Ds[2][FWD_BN];
     __shared__ __attribute__((aligned(16))) uint32_t Mb[NW][FWD_BN];   // per wave: key -> position bits
 
@@ -674,8 +677,8 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const int c = tid + i * NT, row = c >> 4, d0 = (c & 15) * 8;
-            *reinterpret_cast<u32x4*>(&Kh[slot][swz_off(row, d0)]) = kreg[i];
-            *reinterpret_cast<u32x4*>(&Vh[slot][swz_off(row, d0)]) = vreg[i];
+            *reinterpret_cast<u32x4*>(&Kh[slot][row * KLD + d0]) = kreg[i];
+            *reinterpret_cast<u32x4*>(&Vh[slot][row * VLD + d0]) = vreg[i];
         }
         if (!SPARSE && tid < FWD_BN) Ds[slot][tid] = dzero ? int4{0, 0, 0, 0} : dreg;
     };
@@ -711,8 +714,8 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
             }
             mfma_pipelined<16>(
                 [&](int i) {
-                    const int off = swz_off(kb * 32 + l32, 16 * (i >> 1) + 8 * hf);
-                    return *reinterpret_cast<const u32x4*>(((i & 1) ? vt : kt) + off);
+                    const int r = kb * 32 + l32, c = 16 * (i >> 1) + 8 * hf;
+                    return *reinterpret_cast<const u32x4*>((i & 1) ? vt + r * VLD + c : kt + r * KLD + c);
                 },
                 [&](int i, u32x4 op) {
                     if (i & 1) dpt = mfma32h(as_f16x8(op), df[i >> 1], dpt);
@@ -753,7 +756,7 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
             mfma_pipelined<8>(
                 [&](int i) {
                     const int k0 = kb * 32 + 16 * (i & 1) + 4 * hf;
-                    return tr_rows_swz(kt, k0, k0 + 8, (i >> 1) * 32, lane);
+                    return tr_rows_ld(kt, KLD, k0, k0 + 8, (i >> 1) * 32, lane);
                 },
                 [&](int i, u32x4 op) { acc[i >> 1] = mfma32h(as_f16x8(op), sb[i & 1], acc[i >> 1]); });
         }

@@ -173,6 +173,18 @@ __device__ __forceinline__ f16x8 tr_operand_swz(const _Float16* M, int r_lo, int
     return as_f16x8(tr_rows_swz(M, r_lo, r_hi, c0, lane));
 }
 
+// A operand (32 rows x 16 k) of 16-bit elements whose row m = lane % 32 is column c0 + m
+// of the row-major [rows][ld] matrix M; k-slots e = 0..3 are rows r_lo + e, e = 4..7 rows
+// r_hi + e - 4 (callers fold the lane half into r_lo / r_hi).
+__device__ __forceinline__ u32x4 tr_rows_ld(const void* Mv, int ld, int r_lo, int r_hi, int c0, int lane) {
+    const uint16_t* M = static_cast<const uint16_t*>(Mv);
+    const int s = lane & 15;
+    const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (s & 3);
+    const u32x2 lo = ds_read_tr16(M + (r_lo + (s >> 2)) * ld + col);
+    const u32x2 hi = ds_read_tr16(M + (r_hi + (s >> 2)) * ld + col);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
 // Round an offset up to 256 bytes.
 __host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 

@@ -48,17 +48,6 @@ struct FwdArgs {
 constexpr int K_LD = HEAD_DIM + 8;    // bf16 per K row in LDS
 constexpr int V_LD = HEAD_DIM + 16;   // bf16 per V row in LDS
 
-// A operand (32 rows x 16 k) of 16-bit elements whose row m = lane % 32 is column c0 + m
-// of the row-major [rows][ld] matrix M; k-slots e = 0..3 are rows r_lo + e, e = 4..7 rows
-// r_hi + e - 4 (callers fold the lane half into r_lo / r_hi).
-__device__ __forceinline__ u32x4 tr_rows_ld(const bf16* M, int ld, int r_lo, int r_hi, int c0, int lane) {
-    const int s = lane & 15;
-    const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (s & 3);
-    const u32x2 lo = ds_read_tr16(M + (r_lo + (s >> 2)) * ld + col);
-    const u32x2 hi = ds_read_tr16(M + (r_hi + (s >> 2)) * ld + col);
-    return u32x4{lo[0], lo[1], hi[0], hi[1]};
-}
-
 // Block-sparse work items: one (query head, query block) row of the keep matrix, b/32
 // waves, each list entry a b-key block walked as b/64 tiles. K and V are staged row-major
 // (V^T read with transposed LDS reads, as in the dense kernel), single-buffered with two
