@@ -261,8 +261,17 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
     constexpr int KEYS = NWK * 32;
     constexpr int CPT = 512 / NR;         // 16-byte chunks per thread per staged row block
 
-    __shared__ __attribute__((aligned(16))) _Float16 Qh[3][32 * HEAD_DIM];    // swizzled rows
-    __shared__ __attribute__((aligned(16))) _Float16 dOh[2][32 * HEAD_DIM];   // swizzled rows
+    // staged rows: skewed (512-byte pitch) for 4 key blocks; the XOR swizzle (256-byte rows)
+    // for 2, whose smaller LDS footprint keeps two work items per CU
+    constexpr bool SKEW = NWK == 4;
+    constexpr int PITCH = SKEW ? SKEW_PITCH : HEAD_DIM;
+    __shared__ __attribute__((aligned(16))) _Float16 Qh[3][32 * PITCH];
+    __shared__ __attribute__((aligned(16))) _Float16 dOh[2][32 * PITCH];
+    auto roff = [](int q, int col) { return SKEW ? skew_off(q, col) : swz_off(q, col); };
+    auto rtr = [](const _Float16* M, int rb16, int c0, int ln) {
+        if constexpr (SKEW) return tr_rows_skew(M, rb16, c0, ln);
+        else return tr_rows_swz(M, rb16 + 4 * (ln >> 5), rb16 + 8 + 4 * (ln >> 5), c0, ln);
+    };
     __shared__ __attribute__((aligned(16))) _Float16 Ps[2][NWK * 2 * 64 * 8]; // [kb][kk][lane][8]
     __shared__ __attribute__((aligned(16))) float lse_s[3][32];
     __shared__ __attribute__((aligned(16))) float dd_s[2][32];
@@ -359,7 +368,7 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const int c = rt + i * NR;
-            *reinterpret_cast<u32x4*>(&dst[swz_off(c >> 4, (c & 15) * 8)]) = pre[i];
+            *reinterpret_cast<u32x4*>(&dst[roff(c >> 4, (c & 15) * 8)]) = pre[i];
         }
         if (rt < 32) {
             if (is_a)
@@ -377,7 +386,7 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
         for (int r = 0; r < 16; ++r) sacc[r] = 0.f;
         const _Float16* qh = Qh[qs];
         mfma_pipelined<8>(
-            [&](int ks) { return *reinterpret_cast<const u32x4*>(&qh[swz_off(l32, 16 * ks + 8 * hf)]); },
+            [&](int ks) { return *reinterpret_cast<const u32x4*>(&qh[roff(l32, 16 * ks + 8 * hf)]); },
             [&](int ks, u32x4 op) { sacc = mfma32h(as_f16x8(op), kvf[ks], sacc); });
         const bool full = SPARSE ? true : ((e & 1) != 0);
         const bool all_vis = full && key_base + KEYS <= T;   // no element of the step masked
@@ -474,7 +483,7 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
             // dV^T += (dO * sO)^T P of this step
             const _Float16* doh = dOh[step & 1];
             mfma_pipelined<8>(
-                [&](int i) { return tr_rows_swz(doh, 16 * (i & 1) + 4 * hf, 16 * (i & 1) + 8 + 4 * hf, (i >> 1) * 32, lane); },
+                [&](int i) { return rtr(doh, 16 * (i & 1), (i >> 1) * 32, lane); },
                 [&](int i, u32x4 op) { acc[i >> 1] = mfma32h(as_f16x8(op), pb_cur[i & 1], acc[i >> 1]); });
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) pb_cur[kk] = pb_next[kk];
@@ -495,7 +504,7 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
             for (int r = 0; r < 16; ++r) dpacc[r] = 0.f;
             const _Float16* doh = dOh[cb];
             mfma_pipelined<8>(
-                [&](int ks) { return *reinterpret_cast<const u32x4*>(&doh[swz_off(l32, 16 * ks + 8 * hf)]); },
+                [&](int ks) { return *reinterpret_cast<const u32x4*>(&doh[roff(l32, 16 * ks + 8 * hf)]); },
                 [&](int ks, u32x4 op) { dpacc = mfma32h(as_f16x8(op), kvf[ks], dpacc); });
 
             // dS * sO = P * (dP * sO - D * sO); dK^T += (Q * sQ)^T (dS * sO)
@@ -525,7 +534,7 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
             }
             const _Float16* qh = Qh[qs0];
             mfma_pipelined<8>(
-                [&](int i) { return tr_rows_swz(qh, 16 * (i & 1) + 4 * hf, 16 * (i & 1) + 8 + 4 * hf, (i >> 1) * 32, lane); },
+                [&](int i) { return rtr(qh, 16 * (i & 1), (i >> 1) * 32, lane); },
                 [&](int i, u32x4 op) { acc[i >> 1] = mfma32h(as_f16x8(op), sb[i & 1], acc[i >> 1]); });
             if (step + 1 < nsteps) store_rows(cb ^ 1);
             if (step + 2 < nsteps) load_rows(step + 2);

@@ -185,6 +185,27 @@ __device__ __forceinline__ u32x4 tr_rows_ld(const void* Mv, int ld, int r_lo, in
     return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
+// Staged row blocks with a per-row skew instead of the XOR swizzle: row q of 128 fp16
+// starts at element 256 q + 8 (4 (q mod 4) + (q / 4) mod 4), its 16-byte chunks in order,
+// so a row takes 512 bytes of LDS. The skew puts 16 consecutive rows of one chunk, and a
+// 4-row x 4-chunk block, on distinct banks (as the swizzle does), while every operand
+// address is a per-lane row base plus a compile-time chunk offset.
+constexpr int SKEW_PITCH = 256;
+__device__ __forceinline__ int skew_off(int q, int col) {
+    return q * SKEW_PITCH + 8 * (4 * (q & 3) + ((q >> 2) & 3)) + col;
+}
+// tr_rows_swz for a skewed block, with r_lo = rb16 + 4 hf, r_hi = r_lo + 8 (rb16 a
+// multiple of 16): the skew of rows r_lo + s / 4 and r_hi + s / 4 depends on the lane only.
+__device__ __forceinline__ u32x4 tr_rows_skew(const void* Mv, int rb16, int c0, int lane) {
+    const uint16_t* M = static_cast<const uint16_t*>(Mv);
+    const int s = lane & 15, g = (lane >> 4) & 1, hf = lane >> 5;
+    const int lanepart = (4 * hf + (s >> 2)) * SKEW_PITCH + 8 * (4 * (s >> 2) + hf) + 16 * g + 4 * (s & 3);
+    const uint16_t* p = M + lanepart + rb16 * SKEW_PITCH + c0;
+    const u32x2 lo = ds_read_tr16(p);
+    const u32x2 hi = ds_read_tr16(p + 8 * SKEW_PITCH + 16);
+    return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
 // Round an offset up to 256 bytes.
 __host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
