@@ -1,6 +1,6 @@
 // Masked attention backward for gfx950.
 //
-//   D_i  = sum_c dO[i, c] O[i, c]                              (bwd_pre_kernel, HBM-bound)
+//   D_i  = sum_c dO[i, c] O[i, c]                              (bwd_stats_kernel, HBM-bound)
 //   P    = exp(scale * Q K^T - LSE)  on the non-empty tiles    (recomputed)
 //   dV  += P^T dO,  dP = dO V^T,  dS = P * (dP - D)
 //   dK  += scale * dS^T Q                                      (bwd_kernel, key-tile major)
@@ -93,90 +93,84 @@ __device__ __forceinline__ void atomic_max_nonneg(float* p, float v) {
         atomicMax(reinterpret_cast<unsigned int*>(p), __float_as_uint(v));
 }
 
-// Max over the workgroup (blockDim.x = 256), then one conditional atomic per workgroup.
-__device__ __forceinline__ void block_max_to(float* p, float v) {
-    __shared__ float part[4];
-    v = wave_max(v);
-    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
-    __syncthreads();
-    if (threadIdx.x == 0) atomic_max_nonneg(p, fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3])));
-}
-
-// The bound slots = 0 (a kernel rather than a memset, so the sequence can be captured).
+// The four bound slots = 0 (a kernel rather than a memset, so the sequence can be captured).
 __global__ void zero_stats_kernel(float* __restrict__ stats) {
     if (threadIdx.x < BWD_STATS) stats[threadIdx.x] = 0.f;
 }
 
-// D[h][i] = sum_c dO[i][h][c] * (O + O_lo)[i][h][c], and max_i ||dO_i||^2.
-// 16 lanes per (position, head) row; a grid-stride loop over groups of 16 rows, so the
-// per-workgroup maximum reaches the single bound slot with few atomics. The loop bound is
-// uniform over the workgroup, so every lane reaches the shuffles.
-__global__ __launch_bounds__(256) void bwd_pre_kernel(const bf16* __restrict__ o, const bf16* __restrict__ o_lo,
-                                                      const bf16* __restrict__ dout, float* __restrict__ dbuf,
-                                                      float* __restrict__ stats, int T, int Hq) {
-    const long nrows = (long)T * Hq;
+// One pass over the rows of O, O_lo, dO, Q ([T][Hq][128]) and of K, V ([T][Hk][128]):
+//   D[h][i] = sum_c dO[i][h][c] * (O + O_lo)[i][h][c],
+//   the bounds max_i ||dO_i||^2, max |Q|, max |K|, max_j ||V_j||^2.
+// 16 lanes per row, grid-stride loops over groups of 16 rows (their bounds are uniform over
+// the workgroup, so every lane reaches the shuffles); each workgroup then reduces its four
+// maxima and adds them to the slots with one conditional atomic each.
+__global__ __launch_bounds__(256) void bwd_stats_kernel(const bf16* __restrict__ o, const bf16* __restrict__ o_lo,
+                                                        const bf16* __restrict__ dout, const bf16* __restrict__ q,
+                                                        const bf16* __restrict__ k, const bf16* __restrict__ v,
+                                                        float* __restrict__ dbuf, float* __restrict__ stats, int T,
+                                                        int Hq, int Hk) {
     const int part = threadIdx.x & 15;
-    float best = 0.f;
-    for (long base = (long)blockIdx.x * 16; base < nrows; base += (long)gridDim.x * 16) {
+    float b_do = 0.f, b_q = 0.f, b_k = 0.f, b_v = 0.f;
+    const long nq = (long)T * Hq, nk = (long)T * Hk;
+    for (long base = (long)blockIdx.x * 16; base < nq; base += (long)gridDim.x * 16) {
         const long row = base + (threadIdx.x >> 4);
-        float s = 0.f, n2 = 0.f;
-        if (row < nrows) {
-            const u32x4 x = *reinterpret_cast<const u32x4*>(o + row * HEAD_DIM + part * 8);
-            const u32x4 y = *reinterpret_cast<const u32x4*>(dout + row * HEAD_DIM + part * 8);
+        float sd = 0.f, n2 = 0.f;
+        if (row < nq) {
+            const size_t off = (size_t)row * HEAD_DIM + part * 8;
+            const u32x4 x = *reinterpret_cast<const u32x4*>(o + off);
+            const u32x4 y = *reinterpret_cast<const u32x4*>(dout + off);
+            const u32x4 qq = *reinterpret_cast<const u32x4*>(q + off);
             u32x4 z = {0u, 0u, 0u, 0u};
-            if (o_lo) z = *reinterpret_cast<const u32x4*>(o_lo + row * HEAD_DIM + part * 8);
+            if (o_lo) z = *reinterpret_cast<const u32x4*>(o_lo + off);
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const float d0 = bf16_lo(y[m]), d1 = bf16_hi(y[m]);
-                s += d0 * (bf16_lo(x[m]) + bf16_lo(z[m])) + d1 * (bf16_hi(x[m]) + bf16_hi(z[m]));
+                sd += d0 * (bf16_lo(x[m]) + bf16_lo(z[m])) + d1 * (bf16_hi(x[m]) + bf16_hi(z[m]));
                 n2 += d0 * d0 + d1 * d1;
+                b_q = fmaxf(b_q, fmaxf(fabsf(bf16_lo(qq[m])), fabsf(bf16_hi(qq[m]))));
             }
         }
 #pragma unroll
         for (int off = 8; off >= 1; off >>= 1) {
-            s += __shfl_xor(s, off);
+            sd += __shfl_xor(sd, off);
             n2 += __shfl_xor(n2, off);
         }
-        if (part == 0 && row < nrows) {
+        if (part == 0 && row < nq) {
             const int pos = (int)(row / Hq), head = (int)(row % Hq);
-            dbuf[(size_t)head * T + pos] = s;
+            dbuf[(size_t)head * T + pos] = sd;
         }
-        best = fmaxf(best, n2);
+        b_do = fmaxf(b_do, n2);
     }
-    block_max_to(stats + ST_DO_NORM2, best);
-}
-
-// max |x| over n8 chunks of 8 bf16.
-__global__ __launch_bounds__(256) void maxabs_kernel(const u32x4* __restrict__ p, size_t n8,
-                                                     float* __restrict__ out) {
-    float m = 0.f;
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += (size_t)gridDim.x * blockDim.x) {
-        const u32x4 x = p[i];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) m = fmaxf(m, fmaxf(fabsf(bf16_lo(x[j])), fabsf(bf16_hi(x[j]))));
-    }
-    block_max_to(out, m);
-}
-
-// max over rows of the squared norm of 128-element bf16 rows; 16 lanes per row, the
-// loop bound is uniform over the workgroup so every lane reaches the shuffles.
-__global__ __launch_bounds__(256) void rownorm_kernel(const bf16* __restrict__ p, long nrows,
-                                                      float* __restrict__ out) {
-    float best = 0.f;
-    const int part = threadIdx.x & 15;
-    for (long base = (long)blockIdx.x * 16; base < nrows; base += (long)gridDim.x * 16) {
+    for (long base = (long)blockIdx.x * 16; base < nk; base += (long)gridDim.x * 16) {
         const long row = base + (threadIdx.x >> 4);
         float n2 = 0.f;
-        if (row < nrows) {
-            const u32x4 x = *reinterpret_cast<const u32x4*>(p + row * HEAD_DIM + part * 8);
+        if (row < nk) {
+            const size_t off = (size_t)row * HEAD_DIM + part * 8;
+            const u32x4 kk = *reinterpret_cast<const u32x4*>(k + off);
+            const u32x4 vv = *reinterpret_cast<const u32x4*>(v + off);
 #pragma unroll
-            for (int m = 0; m < 4; ++m) n2 += bf16_lo(x[m]) * bf16_lo(x[m]) + bf16_hi(x[m]) * bf16_hi(x[m]);
+            for (int m = 0; m < 4; ++m) {
+                b_k = fmaxf(b_k, fmaxf(fabsf(bf16_lo(kk[m])), fabsf(bf16_hi(kk[m]))));
+                n2 += bf16_lo(vv[m]) * bf16_lo(vv[m]) + bf16_hi(vv[m]) * bf16_hi(vv[m]);
+            }
         }
 #pragma unroll
         for (int off = 8; off >= 1; off >>= 1) n2 += __shfl_xor(n2, off);
-        best = fmaxf(best, n2);
+        b_v = fmaxf(b_v, n2);
     }
-    block_max_to(out, best);
+    // workgroup maxima (blockDim.x = 256, 4 waves), one conditional atomic per slot
+    __shared__ float part_max[4][4];
+    const float vals[4] = {wave_max(b_do), wave_max(b_v), wave_max(b_q), wave_max(b_k)};
+    if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) part_max[j][threadIdx.x >> 6] = vals[j];
+    }
+    __syncthreads();
+    if (threadIdx.x < 4) {
+        const int j = threadIdx.x;   // ST_DO_NORM2, ST_V_NORM2, ST_Q_ABS, ST_K_ABS
+        const float m = fmaxf(fmaxf(part_max[j][0], part_max[j][1]), fmaxf(part_max[j][2], part_max[j][3]));
+        atomic_max_nonneg(stats + j, m);
+    }
 }
 
 // 8 bf16 (one 16-byte chunk) -> 8 fp16 scaled by s.
@@ -797,18 +791,12 @@ hipError_t launch_bwd_pre(const Problem& P, const void* q, const void* k, const 
     char* ws = reinterpret_cast<char*>(dbuf);
     float* stats = reinterpret_cast<float*>(ws + W.stats);
     hipLaunchKernelGGL(zero_stats_kernel, dim3(1), dim3(64), 0, s, stats);
-    const long rows = (long)P.T * P.Hq;
-    const long groups = (rows + 15) / 16;
-    hipLaunchKernelGGL(bwd_pre_kernel, dim3((unsigned)(groups < 4096 ? groups : 4096)), dim3(256), 0, s,
+    const long groups = ((long)P.T * P.Hq + 15) / 16;
+    hipLaunchKernelGGL(bwd_stats_kernel, dim3((unsigned)(groups < 4096 ? groups : 4096)), dim3(256), 0, s,
                        static_cast<const bf16*>(o), static_cast<const bf16*>(o_lo), static_cast<const bf16*>(dout),
-                       dbuf, stats, P.T, P.Hq);
+                       static_cast<const bf16*>(q), static_cast<const bf16*>(k), static_cast<const bf16*>(v), dbuf,
+                       stats, P.T, P.Hq, P.Hk);
     const size_t nq8 = (size_t)P.T * P.Hq * HEAD_DIM / 8, nk8 = (size_t)P.T * P.Hk * HEAD_DIM / 8;
-    hipLaunchKernelGGL(maxabs_kernel, dim3(1024), dim3(256), 0, s, static_cast<const u32x4*>(q), nq8,
-                       stats + ST_Q_ABS);
-    hipLaunchKernelGGL(maxabs_kernel, dim3(256), dim3(256), 0, s, static_cast<const u32x4*>(k), nk8,
-                       stats + ST_K_ABS);
-    hipLaunchKernelGGL(rownorm_kernel, dim3(256), dim3(256), 0, s, static_cast<const bf16*>(v),
-                       (long)P.T * P.Hk, stats + ST_V_NORM2);
     hipLaunchKernelGGL(to_f16_kernel, dim3(2048), dim3(256), 0, s, static_cast<const u32x4*>(q),
                        static_cast<const u32x4*>(dout), static_cast<const u32x4*>(k), static_cast<const u32x4*>(v),
                        reinterpret_cast<u32x4*>(ws + W.qh), reinterpret_cast<u32x4*>(ws + W.doh),
