@@ -573,7 +573,10 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
     constexpr int TPE = SPARSE ? NW / 2 : 1;     // 64-key tiles per list entry
 
     // Padded rows (fp16 per row): K is read as rows (S^T) and transposed (dQ^T), V as rows
-    // only; these strides measured faster than the XOR swizzle of the staged backward rows.
+    // only. Every operand read is a per-lane base plus a compile-time offset, which measured
+    // faster than an XOR swizzle of 256-byte rows (whose lane-dependent addresses cost
+    // vector instructions), although K at this stride is not free of bank conflicts for both
+    // read patterns.
     constexpr int KLD = HEAD_DIM + 16, VLD = HEAD_DIM + 8;
     __shared__ __attribute__((aligned(16))) _Float16 Kh[2][FWD_BN * KLD];
     __shared__ __attribute__((aligned(16))) _Float16 Vh[2][FWD_BN * VLD];
