@@ -241,11 +241,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_sparse_kernel(FwdArgs a) {
 //    when the running max has to move (the lazy rescale).
 __global__ __launch_bounds__(512) void fwd_dense_kernel(FwdArgs a) {
     constexpr int NT = 512;
-    constexpr int CPT = 1024 / NT;   // 16-byte chunks per thread per tile per tensor
+    constexpr int SUB = 2;                   // list entries (64-key tiles) staged together
+    constexpr int CPT = SUB * 1024 / NT;     // 16-byte chunks per thread per stage per tensor
 
-    __shared__ __attribute__((aligned(16))) bf16 Kb[2][FWD_BN * K_LD];
-    __shared__ __attribute__((aligned(16))) bf16 Vb[2][FWD_BN * V_LD];
-    __shared__ int4 Db[2][FWD_BN];
+    __shared__ __attribute__((aligned(16))) bf16 Kb[2][SUB * FWD_BN * K_LD];
+    __shared__ __attribute__((aligned(16))) bf16 Vb[2][SUB * FWD_BN * V_LD];
+    __shared__ int4 Db[2][SUB * FWD_BN];
     __shared__ __attribute__((aligned(16))) uint32_t Mb[8][FWD_BN];   // per wave: key -> position bits
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -291,50 +292,61 @@ __global__ __launch_bounds__(512) void fwd_dense_kernel(FwdArgs a) {
 
     EntryStream es;
     es.init(a.ent, lb, n, lane);
-    int e_cur = 0, e_nxt = 0;   // entries of tiles t and t + 1
+    // A stage is SUB consecutive list entries (the last stage may hold fewer; its missing
+    // entries repeat the last one and are not computed); e_cur / e_nxt hold the entries of
+    // stages u and u + 1.
+    const int nst = (n + SUB - 1) / SUB;
+    int e_cur[SUB] = {}, e_nxt[SUB] = {};
 
     // Rows past the end are read from row T - 1 (finite data; such keys are masked).
     u32x4 kreg[CPT], vreg[CPT];
     int4 dreg = {0, 0, 0, 0};
     bool dzero = false;
-    auto load_tile = [&](int t) {
-        const int e = es.get(t, lane);
-        e_cur = e_nxt;
-        e_nxt = e;
-        const int key0 = (e >> 1) * FWD_BN;
+    auto load_stage = [&](int u) {
+#pragma unroll
+        for (int sb = 0; sb < SUB; ++sb) {
+            e_cur[sb] = e_nxt[sb];
+            const int t = SUB * u + sb;
+            e_nxt[sb] = t < n ? es.get(t, lane) : e_nxt[sb > 0 ? sb - 1 : 0];
+        }
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
-            const int c = tid + i * NT, key = min(key0 + (c >> 4), T - 1);
-            const size_t o = (size_t)key * kv_row + (c & 15) * 8;
+            const int c = tid + i * NT, sb = (i * NT) >> 10, cc = c & 1023;
+            const int key = min((e_nxt[sb] >> 1) * FWD_BN + (cc >> 4), T - 1);
+            const size_t o = (size_t)key * kv_row + (cc & 15) * 8;
             kreg[i] = *reinterpret_cast<const u32x4*>(kbase + o);
             vreg[i] = *reinterpret_cast<const u32x4*>(vbase + o);
         }
-        if (tid < FWD_BN) {
-            const int key = key0 + tid;
+        if (tid < SUB * FWD_BN) {
+            const int sb = tid / FWD_BN;
+            const int key = (e_nxt[sb] >> 1) * FWD_BN + (tid % FWD_BN);
             dreg = a.desc[min(key, T - 1)];
             dzero = key >= T;
         }
     };
-    auto store_tile = [&](int slot) {
+    auto store_stage = [&](int slot) {
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const int c = tid + i * NT, row = c >> 4, col = (c & 15) * 8;
             *reinterpret_cast<u32x4*>(&Kb[slot][row * K_LD + col]) = kreg[i];
             *reinterpret_cast<u32x4*>(&Vb[slot][row * V_LD + col]) = vreg[i];
         }
-        if (tid < FWD_BN) Db[slot][tid] = dzero ? int4{0, 0, 0, 0} : dreg;
+        if (tid < SUB * FWD_BN) Db[slot][tid] = dzero ? int4{0, 0, 0, 0} : dreg;
     };
 
-    if (n > 0) {
-        load_tile(0);
-        store_tile(0);
-        if (n > 1) load_tile(1);
+    if (nst > 0) {
+        load_stage(0);
+        store_stage(0);
+        if (nst > 1) load_stage(1);
     }
     lds_barrier();
 
-    for (int t = 0; t < n; ++t) {
-        const int cb = t & 1;
-        const int e = t + 1 < n ? e_cur : e_nxt;
+    for (int u = 0; u < nst; ++u) {
+      const int cb = u & 1;
+#pragma unroll
+      for (int sb = 0; sb < SUB; ++sb) {
+        if (SUB * u + sb >= n) break;
+        const int e = u + 1 < nst ? e_cur[sb] : e_nxt[sb];
         const int key0 = (e >> 1) * FWD_BN;
         const bool need_mask = (e & 1) == 0 || key0 + FWD_BN > T;
 
@@ -344,7 +356,7 @@ __global__ __launch_bounds__(512) void fwd_dense_kernel(FwdArgs a) {
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-        const bf16* kr = Kb[cb] + l32 * K_LD + 8 * hf;
+        const bf16* kr = Kb[cb] + (sb * FWD_BN + l32) * K_LD + 8 * hf;
         mfma_pipelined<16>(
             [&](int i) { return *reinterpret_cast<const u32x4*>(kr + (i & 1) * 32 * K_LD + 16 * (i >> 1)); },
             [&](int i, u32x4 op) { s[i & 1] = mfma32(as_bf16x8(op), qf[i >> 1], s[i & 1]); });
@@ -353,7 +365,7 @@ __global__ __launch_bounds__(512) void fwd_dense_kernel(FwdArgs a) {
             // Lane j turns key j's two row intervals into a bit mask over the wave's (at
             // most 32) distinct positions p_base .. p_base + 31; every lane then tests its
             // own position's bit in the masks of the 32 keys it holds.
-            const int4 d = Db[cb][lane];
+            const int4 d = Db[cb][sb * FWD_BN + lane];
             Mb[w][lane] = interval_bits(d.x, d.y, p_base) | interval_bits(d.z, d.w, p_base);
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's masks written
 #pragma unroll
@@ -406,7 +418,7 @@ __global__ __launch_bounds__(512) void fwd_dense_kernel(FwdArgs a) {
         }
 
         // O^T += V^T P^T: key slot (hf, e) of step kk is key 16*kk + 8*(e/4) + 4*hf + e%4.
-        const bf16* vt = Vb[cb];
+        const bf16* vt = Vb[cb] + sb * FWD_BN * V_LD;
         mfma_pipelined<16>(
             [&](int i) {
                 const int kk = i >> 2, db = i & 3;
@@ -414,10 +426,11 @@ __global__ __launch_bounds__(512) void fwd_dense_kernel(FwdArgs a) {
             },
             [&](int i, u32x4 op) { acc[i & 3] = mfma32(as_bf16x8(op), pb[i >> 2], acc[i & 3]); });
 
-        // tile t + 1 into the other slot (its readers of tile t - 1 passed the last
-        // barrier), loads of tile t + 2
-        if (t + 1 < n) store_tile(cb ^ 1);
-        if (t + 2 < n) load_tile(t + 2);
+      }
+        // stage u + 1 into the other slot (its readers of stage u - 1 passed the last
+        // barrier), loads of stage u + 2
+        if (u + 1 < nst) store_stage(cb ^ 1);
+        if (u + 2 < nst) load_stage(u + 2);
         lds_barrier();
     }
 
