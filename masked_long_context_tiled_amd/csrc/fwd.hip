@@ -231,9 +231,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_sparse_kernel(FwdArgs a) {
 
 // Dense work items (the G heads of one KV head x 256/G positions, 8 waves of 32 rows).
 // Same arithmetic as fwd_sparse_kernel, with these differences:
-//  - K, V and the column descriptors are double-buffered in LDS: while tile t is
-//    computed from slot t % 2, tile t + 1 (loaded one tile earlier) is stored into the
-//    other slot and the loads of tile t + 2 are issued; one barrier per tile;
+//  - K, V and the column descriptors are double-buffered in LDS by stages of two
+//    64-key tiles (two list entries): while stage u is computed from slot u % 2, stage
+//    u + 1 (loaded one stage earlier) is stored into the other slot and the loads of stage
+//    u + 2 are issued; one barrier per stage;
 //  - PARTIAL tiles are masked through per-key bit masks over the wave's positions;
 //  - list entries are read from registers filled a chunk ahead, so no load waits on a
 //    freshly loaded entry;
