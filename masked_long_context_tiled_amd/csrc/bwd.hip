@@ -471,16 +471,14 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
         // or of steps s and s + 1 when s + 2 is past the end.
         int qs1 = 1;   // Q slot of step s + 1
         for (int step = 0; step < nsteps; ++step) {
-            f16x8 pb_next[2];
-            if (step + 1 < nsteps) s_and_p(step + 1, step + 2 < nsteps ? e_q0 : e_q1, qs1, pb_next);
-
-            // dV^T += (dO * sO)^T P of this step
+            // dV^T += (dO * sO)^T P of this step first (P from the previous step), then S and
+            // P of the next step: the exponentials then run while the B wave on the same SIMD
+            // issues its dK MFMAs, and B's dS work while this wave issues MFMAs
             const _Float16* doh = dOh[step & 1];
             mfma_pipelined<8>(
                 [&](int i) { return rtr(doh, 16 * (i & 1), (i >> 1) * 32, lane); },
                 [&](int i, u32x4 op) { acc[i >> 1] = mfma32h(as_f16x8(op), pb_cur[i & 1], acc[i >> 1]); });
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) pb_cur[kk] = pb_next[kk];
+            if (step + 1 < nsteps) s_and_p(step + 1, step + 2 < nsteps ? e_q0 : e_q1, qs1, pb_cur);
 
             const int qs2 = qs1 == 2 ? 0 : qs1 + 1;   // Q slot of step s + 2
             if (step + 2 < nsteps) store_rows(qs2);
