@@ -103,7 +103,7 @@ __global__ void zero_stats_kernel(float* __restrict__ stats) {
 //   the bounds max_i ||dO_i||^2, max |Q|, max |K|, max_j ||V_j||^2.
 // 16 lanes per row, grid-stride loops over groups of 16 rows (their bounds are uniform over
 // the workgroup, so every lane reaches the shuffles); each workgroup then reduces its four
-// maxima and adds them to the slots with one conditional atomic each.
+// maxima and raises the slots to them with one conditional atomic max each.
 __global__ __launch_bounds__(256) void bwd_stats_kernel(const bf16* __restrict__ o, const bf16* __restrict__ o_lo,
                                                         const bf16* __restrict__ dout, const bf16* __restrict__ q,
                                                         const bf16* __restrict__ k, const bf16* __restrict__ v,
