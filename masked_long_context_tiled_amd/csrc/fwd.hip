@@ -303,6 +303,14 @@ __global__ __launch_bounds__(512) void fwd_dense_kernel(FwdArgs a) {
     u32x4 kreg[CPT], vreg[CPT];
     int4 dreg = {0, 0, 0, 0};
     bool dzero = false;
+    // the fixed part of each chunk's offset: chunk c = tid + i * NT is row (c % 1024) / 16 of
+    // its sub-tile, dims 8 (c % 16) .. + 7
+    unsigned lofs[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const int cc = (tid + i * NT) & 1023;
+        lofs[i] = (unsigned)((cc >> 4) * kv_row + (cc & 15) * 8);
+    }
     auto load_stage = [&](int u) {
 #pragma unroll
         for (int sb = 0; sb < SUB; ++sb) {
@@ -311,12 +319,27 @@ __global__ __launch_bounds__(512) void fwd_dense_kernel(FwdArgs a) {
             e_nxt[sb] = t < n ? es.get(t, lane) : e_nxt[sb > 0 ? sb - 1 : 0];
         }
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int c = tid + i * NT, sb = (i * NT) >> 10, cc = c & 1023;
-            const int key = min((e_nxt[sb] >> 1) * FWD_BN + (cc >> 4), T - 1);
-            const size_t o = (size_t)key * kv_row + (cc & 15) * 8;
-            kreg[i] = *reinterpret_cast<const u32x4*>(kbase + o);
-            vreg[i] = *reinterpret_cast<const u32x4*>(vbase + o);
+        for (int sb = 0; sb < SUB; ++sb) {
+            const int key0 = __builtin_amdgcn_readfirstlane((e_nxt[sb] >> 1) * FWD_BN);   // uniform
+            if (key0 + FWD_BN <= T) {
+                // a whole tile: scalar tile base plus the lane's fixed 32-bit offset
+                const bf16* kt0 = kbase + (size_t)key0 * kv_row;
+                const bf16* vt0 = vbase + (size_t)key0 * kv_row;
+#pragma unroll
+                for (int i = sb * (CPT / SUB); i < (sb + 1) * (CPT / SUB); ++i) {
+                    kreg[i] = *reinterpret_cast<const u32x4*>(kt0 + lofs[i]);
+                    vreg[i] = *reinterpret_cast<const u32x4*>(vt0 + lofs[i]);
+                }
+            } else {
+#pragma unroll
+                for (int i = sb * (CPT / SUB); i < (sb + 1) * (CPT / SUB); ++i) {
+                    const int cc = (tid + i * NT) & 1023;
+                    const int key = min(key0 + (cc >> 4), T - 1);
+                    const size_t o = (size_t)key * kv_row + (cc & 15) * 8;
+                    kreg[i] = *reinterpret_cast<const u32x4*>(kbase + o);
+                    vreg[i] = *reinterpret_cast<const u32x4*>(vbase + o);
+                }
+            }
         }
         if (tid < SUB * FWD_BN) {
             const int sb = tid / FWD_BN;
