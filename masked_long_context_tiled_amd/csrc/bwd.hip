@@ -649,6 +649,14 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
     u32x4 kreg[CPT], vreg[CPT];
     int4 dreg = {0, 0, 0, 0};
     bool dzero = false;
+    // the fixed part of each chunk's offset: chunk c = tid + i * NT is row c / 16 of the
+    // tile, dims 8 (c % 16) .. + 7
+    unsigned lofs[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const int c = tid + i * NT;
+        lofs[i] = (unsigned)((c >> 4) * kv_row + (c & 15) * 8);
+    }
     auto load_tile = [&](int t) {
         const int e = es.get(t / TPE, lane);
         int key0;
@@ -664,12 +672,24 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
         mask_cur = mask_nxt;
         key0_nxt = key0;
         mask_nxt = !full || key0 + FWD_BN > T;
+        const int k0u = __builtin_amdgcn_readfirstlane(key0);
+        if (k0u + FWD_BN <= T) {
+            // a whole tile: uniform tile base plus the lane's fixed offsets
+            const _Float16* kt0 = kbase + (size_t)k0u * kv_row;
+            const _Float16* vt0 = vbase + (size_t)k0u * kv_row;
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int c = tid + i * NT, key = min(key0 + (c >> 4), T - 1);
-            const size_t o = (size_t)key * kv_row + (c & 15) * 8;
-            kreg[i] = *reinterpret_cast<const u32x4*>(kbase + o);
-            vreg[i] = *reinterpret_cast<const u32x4*>(vbase + o);
+            for (int i = 0; i < CPT; ++i) {
+                kreg[i] = *reinterpret_cast<const u32x4*>(kt0 + lofs[i]);
+                vreg[i] = *reinterpret_cast<const u32x4*>(vt0 + lofs[i]);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) {
+                const int c = tid + i * NT, key = min(key0 + (c >> 4), T - 1);
+                const size_t o = (size_t)key * kv_row + (c & 15) * 8;
+                kreg[i] = *reinterpret_cast<const u32x4*>(kbase + o);
+                vreg[i] = *reinterpret_cast<const u32x4*>(vbase + o);
+            }
         }
         if (!SPARSE && tid < FWD_BN) {
             const int key = key0 + tid;
