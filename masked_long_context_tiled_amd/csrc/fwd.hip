@@ -106,15 +106,37 @@ __global__ __launch_bounds__(NW * 64) void fwd_sparse_kernel(FwdArgs a) {
     // Rows past the end are read from row T - 1 (finite data; such keys are masked).
     u32x4 kreg[CPT], vreg[CPT];
     int nkey0 = 0;
+    // the fixed part of each chunk's offset: chunk c = tid + i * NT is row c / 16 of the
+    // tile, dims 8 (c % 16) .. + 7 (b = 128 only: at b = 64 the eight offsets per thread
+    // would cost the kernel its second wave per SIMD)
+    constexpr bool FIXED_OFS = NW == 4;
+    unsigned lofs[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const int c = tid + i * NT;
+        lofs[i] = FIXED_OFS ? (unsigned)((c >> 4) * kv_row + (c & 15) * 8) : 0u;
+    }
     auto load_tile = [&](int t) {
         const int e = es.get(t / TPE, lane);
-        nkey0 = e * a.sblock + (t % TPE) * FWD_BN;
+        const int k0 = e * a.sblock + (t % TPE) * FWD_BN;
+        nkey0 = FIXED_OFS ? __builtin_amdgcn_readfirstlane(k0) : k0;   // uniform either way
+        if (FIXED_OFS && nkey0 + FWD_BN <= T) {
+            // a whole tile: uniform tile base plus the lane's fixed offsets
+            const bf16* kt0 = kbase + (size_t)nkey0 * kv_row;
+            const bf16* vt0 = vbase + (size_t)nkey0 * kv_row;
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) {
-            const int c = tid + i * NT, key = min(nkey0 + (c >> 4), T - 1);
-            const size_t o = (size_t)key * kv_row + (c & 15) * 8;
-            kreg[i] = *reinterpret_cast<const u32x4*>(kbase + o);
-            vreg[i] = *reinterpret_cast<const u32x4*>(vbase + o);
+            for (int i = 0; i < CPT; ++i) {
+                kreg[i] = *reinterpret_cast<const u32x4*>(kt0 + lofs[i]);
+                vreg[i] = *reinterpret_cast<const u32x4*>(vt0 + lofs[i]);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) {
+                const int c = tid + i * NT, key = min(nkey0 + (c >> 4), T - 1);
+                const size_t o = (size_t)key * kv_row + (c & 15) * 8;
+                kreg[i] = *reinterpret_cast<const u32x4*>(kbase + o);
+                vreg[i] = *reinterpret_cast<const u32x4*>(vbase + o);
+            }
         }
     };
 
