@@ -93,9 +93,12 @@ def test_single_position():
     _check(1, 8, 2, MaskSpec("causal"), seed=9)
 
 
-@pytest.mark.parametrize("b", [64, 128])
-def test_block_sparse(b):
-    T, Hq, Hk = 1000, 8, 2
+@pytest.mark.parametrize("b,T", [(64, 1000), (128, 1000), (64, 936), (128, 936)])
+def test_block_sparse(b, T):
+    # T = 1000: the last block is ragged in its second 64-key half (b = 128) or in its only
+    # half (b = 64); T = 936: at b = 128 the last block's first half is ragged and its second
+    # half lies wholly past the end
+    Hq, Hk = 8, 2
     nb = -(-T // b)
     keep = block_sparse_keep(11, Hq, nb, nb)
     _check(T, Hq, Hk, MaskSpec("block_sparse", sparse_block=b), keep=keep, seed=11)
