@@ -52,11 +52,17 @@ constexpr int V_LD = HEAD_DIM + 16;   // bf16 per V row in LDS
 // waves, each list entry a b-key block walked as b/64 tiles. K and V are staged row-major
 // (V^T read with transposed LDS reads, as in the dense kernel), single-buffered with two
 // barriers per tile (the small LDS footprint keeps four work items per CU).
-template <int NW>
+//
+// PAIR (b = 64, four waves): one work item is query blocks 2p (waves 0, 1) and 2p + 1
+// (waves 2, 3) of one head. It walks the union of their two ascending key lists, so a key
+// block both keep is staged once; each staged tile is computed by the waves whose query
+// block keeps it (the choice is uniform per wave, and the loop's trip count is uniform per
+// work item, so every wave meets every barrier).
+template <int NW, bool PAIR = false>
 __global__ __launch_bounds__(NW * 64) void fwd_sparse_kernel(FwdArgs a) {
     constexpr int NT = NW * 64;
-    constexpr int CPT = 1024 / NT;   // 16-byte chunks per thread per tile per tensor
-    constexpr int TPE = NW / 2;      // 64-key tiles per list entry
+    constexpr int CPT = 1024 / NT;            // 16-byte chunks per thread per tile per tensor
+    constexpr int TPE = PAIR ? 1 : NW / 2;    // 64-key tiles per list entry
 
     __shared__ __attribute__((aligned(16))) bf16 Ks[FWD_BN * K_LD];
     __shared__ __attribute__((aligned(16))) bf16 Vs[FWD_BN * V_LD];
@@ -68,12 +74,19 @@ __global__ __launch_bounds__(NW * 64) void fwd_sparse_kernel(FwdArgs a) {
     const int g = blockIdx.x % a.Hk, y = blockIdx.x / a.Hk;
     const int T = a.T;
 
-    const int hi = y / a.nb, qb = y - hi * a.nb;
+    const int span = PAIR ? (a.nb + 1) >> 1 : a.nb;   // work items per head
+    const int hi = y / span, item = y - hi * span;
+    const int sub = PAIR ? w >> 1 : 0;                // PAIR: which block of the pair
+    const int qb = PAIR ? 2 * item + sub : item;
     const int head = g * a.G + hi;
-    const int pos = qb * a.sblock + w * 32 + l32;
-    const int lb = a.ptr[head * a.nb + qb], le = a.ptr[head * a.nb + qb + 1];
+    const int pos = qb * a.sblock + (PAIR ? (w & 1) : w) * 32 + l32;
+    const int r0 = head * a.nb + (PAIR ? 2 * item : item);
+    // the (first) block's list; PAIR: the second block's list follows it in the CSR and is
+    // empty when the pair's second block lies past the last one
+    const int lb = a.ptr[r0], le = a.ptr[r0 + 1];
+    const int le2 = (PAIR && 2 * item + 1 < a.nb) ? a.ptr[r0 + 2] : le;
     const bool row_ok = pos < T;
-    const int ntiles = (le - lb) * TPE;
+    const int ntiles = (le - lb) * TPE;   // (not PAIR)
 
     // Q row fragments: B operand, lane holds dims 16*ks + 8*hf .. +7 of its row; the loads
     // complete before the loop (left pending, the first wait in the loop would also cover
@@ -100,8 +113,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_sparse_kernel(FwdArgs a) {
 
     // list entries from registers filled a chunk of 64 ahead (no tile waits on a freshly
     // loaded entry before it can address its K/V loads)
-    EntryStream es;
+    EntryStream es, es2;
     es.init(a.ent, lb, le - lb, lane);
+    int ia = 0, ib = 0;                    // PAIR: entries of each list consumed
+    const int na = le - lb, nb2 = le2 - le;
+    if constexpr (PAIR) es2.init(a.ent, le, nb2, lane);
+    bool nka = true, nkb = true;           // PAIR: the loaded tile is kept by block 2p / 2p + 1
 
     // Rows past the end are read from row T - 1 (finite data; such keys are masked).
     u32x4 kreg[CPT], vreg[CPT];
@@ -117,7 +134,19 @@ __global__ __launch_bounds__(NW * 64) void fwd_sparse_kernel(FwdArgs a) {
         lofs[i] = FIXED_OFS ? (unsigned)((c >> 4) * kv_row + (c & 15) * 8) : 0u;
     }
     auto load_tile = [&](int t) {
-        const int e = es.get(t / TPE, lane);
+        int e;
+        if constexpr (PAIR) {
+            // the smaller head of the two lists (uniform: read through readlane)
+            const int ea = ia < na ? es.get(ia, lane) : 0x7fffffff;
+            const int eb = ib < nb2 ? es2.get(ib, lane) : 0x7fffffff;
+            e = min(ea, eb);
+            nka = ea == e;
+            nkb = eb == e;
+            ia += nka;
+            ib += nkb;
+        } else {
+            e = es.get(t / TPE, lane);
+        }
         const int k0 = e * a.sblock + (t % TPE) * FWD_BN;
         nkey0 = FIXED_OFS ? __builtin_amdgcn_readfirstlane(k0) : k0;   // uniform either way
         if (FIXED_OFS && nkey0 + FWD_BN <= T) {
@@ -140,11 +169,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_sparse_kernel(FwdArgs a) {
         }
     };
 
-    if (ntiles > 0) load_tile(0);
+    bool have = PAIR ? na + nb2 > 0 : ntiles > 0;
+    if (have) load_tile(0);
 
-    for (int t = 0; t < ntiles; ++t) {
+    for (int t = 0; have; ++t) {
         const int key0 = nkey0;
         const bool need_mask = key0 + FWD_BN > T;
+        const bool mine = sub == 0 ? nka : nkb;   // PAIR: this wave's block keeps the tile
 
         __syncthreads();   // every wave is done reading the previous tile
 #pragma unroll
@@ -155,7 +186,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_sparse_kernel(FwdArgs a) {
         }
         lds_barrier();
 
-        if (t + 1 < ntiles) load_tile(t + 1);
+        have = PAIR ? (ia < na || ib < nb2) : t + 1 < ntiles;
+        if (have) load_tile(t + 1);
+        if (PAIR && !mine) continue;
 
         // S^T = K Q^T for the two 32-key halves of the tile
         f32x16 s[2];
@@ -536,7 +569,7 @@ hipError_t launch_fwd(const Problem& P, const void* q, const void* k, const void
     if (!P.sparse) {
         hipLaunchKernelGGL(fwd_dense_kernel, dim3(P.Hk * P.nqt_f), dim3(512), 0, s, a);
     } else if (P.sblock == 64) {
-        hipLaunchKernelGGL((fwd_sparse_kernel<2>), dim3(P.Hk * P.G * P.nb), dim3(128), 0, s, a);
+        hipLaunchKernelGGL((fwd_sparse_kernel<4, true>), dim3(P.Hk * P.G * ((P.nb + 1) / 2)), dim3(256), 0, s, a);
     } else {
         hipLaunchKernelGGL((fwd_sparse_kernel<4>), dim3(P.Hk * P.G * P.nb), dim3(256), 0, s, a);
     }
