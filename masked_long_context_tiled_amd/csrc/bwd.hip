@@ -564,11 +564,16 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
 // K, V and the column descriptors are double-buffered in LDS: while tile t is computed
 // from slot t % 2, tile t + 1 (loaded one tile earlier) is stored into the other slot and
 // the loads of tile t + 2 are issued; one barrier per tile.
-template <int NW, bool SPARSE>
+//
+// PAIR (block-sparse, b = 64, four waves): one work item is query blocks 2p (waves 0, 1)
+// and 2p + 1 (waves 2, 3) of one head, walking the union of their two ascending key lists
+// so that a key block both keep is staged once; each staged tile is computed by the waves
+// whose block keeps it (uniform per wave; every wave runs every iteration and barrier).
+template <int NW, bool SPARSE, bool PAIR = false>
 __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
     constexpr int NT = NW * 64;
     constexpr int CPT = 1024 / NT;               // 16-byte chunks per thread per tile per tensor
-    constexpr int TPE = SPARSE ? NW / 2 : 1;     // 64-key tiles per list entry
+    constexpr int TPE = PAIR ? 1 : SPARSE ? NW / 2 : 1;   // 64-key tiles per list entry
 
     // Padded rows (fp16 per row): K is read as rows (S^T) and transposed (dQ^T), V as rows
     // only. Every operand read is a per-lane base plus a compile-time offset, which measured
@@ -591,7 +596,7 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
     const float cS = a.c / (sQ * sK);
     const float inv_sV = 1.f / sV;
 
-    int head, pos, lb, le;
+    int head, pos, lb, le, le2 = 0;
     int p_base = 0;   // the wave's rows cover positions p_base + (0 .. 31) (dense masks)
     if constexpr (!SPARSE) {
         const int qt = a.order[y];
@@ -602,15 +607,20 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
         lb = a.ptr[qt];
         le = a.ptr[qt + 1];
     } else {
-        const int hi = y / a.nb, qb = y - hi * a.nb;
+        const int span = PAIR ? (a.nb + 1) >> 1 : a.nb;   // work items per head
+        const int hi = y / span, item = y - hi * span;
+        const int qb = PAIR ? 2 * item + (w >> 1) : item;
         head = g * a.G + hi;
-        pos = qb * a.sblock + w * 32 + l32;
-        const int r = head * a.nb + qb;
+        pos = qb * a.sblock + (PAIR ? (w & 1) : w) * 32 + l32;
+        const int r = head * a.nb + (PAIR ? 2 * item : item);
         lb = a.ptr[r];
         le = a.ptr[r + 1];
+        // PAIR: the second block's list follows the first's in the CSR; empty when the
+        // pair's second block lies past the last one
+        le2 = (PAIR && 2 * item + 1 < a.nb) ? a.ptr[r + 2] : le;
     }
     const bool row_ok = pos < T;
-    const int ntiles = (le - lb) * TPE;
+    const int ntiles = (le - lb) * TPE;   // (not PAIR: there the union's length is found while walking)
 
     // this lane's row: LSE (base 2), D * sO, Q * sQ and dO * sO as B operands
     float lse2 = INFINITY, dd = 0.f;
@@ -644,6 +654,13 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
     // first key and "needs per-element masking" of tiles t (cur) and t + 1 (nxt)
     int key0_cur = 0, key0_nxt = 0;
     bool mask_cur = false, mask_nxt = false;
+    // PAIR: second list, entries consumed of each list, tiles issued, and whether block 2p
+    // (a) / 2p + 1 (b) keeps tiles t (cur) and t + 1 (nxt)
+    EntryStream es2;
+    const int na = le - lb, nb2 = le2 - le;
+    int ia = 0, ib = 0, issued = 0;
+    if constexpr (PAIR) es2.init(a.ent, le, nb2, lane);
+    bool ka_cur = true, ka_nxt = true, kb_cur = true, kb_nxt = true;
 
     // Rows past the end are read from row T - 1 (finite data; such keys are masked).
     u32x4 kreg[CPT], vreg[CPT];
@@ -658,7 +675,22 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
         lofs[i] = (unsigned)((c >> 4) * kv_row + (c & 15) * 8);
     }
     auto load_tile = [&](int t) {
-        const int e = es.get(t / TPE, lane);
+        int e;
+        if constexpr (PAIR) {
+            // the smaller head of the two lists (uniform: read through readlane)
+            const int ea = ia < na ? es.get(ia, lane) : 0x7fffffff;
+            const int eb = ib < nb2 ? es2.get(ib, lane) : 0x7fffffff;
+            e = min(ea, eb);
+            ka_cur = ka_nxt;
+            kb_cur = kb_nxt;
+            ka_nxt = ea == e;
+            kb_nxt = eb == e;
+            ia += ka_nxt;
+            ib += kb_nxt;
+            ++issued;
+        } else {
+            e = es.get(t / TPE, lane);
+        }
         int key0;
         bool full;
         if constexpr (SPARSE) {
@@ -707,17 +739,21 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
         if (!SPARSE && tid < FWD_BN) Ds[slot][tid] = dzero ? int4{0, 0, 0, 0} : dreg;
     };
 
-    if (ntiles > 0) {
+    // PAIR: entries left in either list (uniform)
+    auto more = [&]() { return ia < na || ib < nb2; };
+    if (PAIR ? more() : ntiles > 0) {
         load_tile(0);
         store_tile(0);
-        if (ntiles > 1) load_tile(1);
+        if (PAIR ? more() : ntiles > 1) load_tile(1);
     }
     lds_barrier();
 
-    for (int t = 0; t < ntiles; ++t) {
+    for (int t = 0; PAIR ? t < issued : t < ntiles; ++t) {
         const int cb = t & 1;
-        const int key0 = t + 1 < ntiles ? key0_cur : key0_nxt;
-        const bool need_mask = t + 1 < ntiles ? mask_cur : mask_nxt;
+        const bool have1 = PAIR ? t + 1 < issued : t + 1 < ntiles;   // tile t + 1 exists
+        const int key0 = have1 ? key0_cur : key0_nxt;
+        const bool need_mask = have1 ? mask_cur : mask_nxt;
+        const bool mine = (w >> 1) == 0 ? (have1 ? ka_cur : ka_nxt) : (have1 ? kb_cur : kb_nxt);
         const _Float16* kt = Kh[cb];
         const _Float16* vt = Vh[cb];
         if (!SPARSE && need_mask) {
@@ -728,66 +764,68 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
         }
         // per 32-key half kb: S^T = K Q^T and dP^T = V dO^T (lane column = its query row,
         // rows = keys), dS^T, then dQ^T += (K * sK)^T (dS^T * sO) for those 32 keys
+        if (!PAIR || mine) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            f32x16 st, dpt;
+            for (int kb = 0; kb < 2; ++kb) {
+                f32x16 st, dpt;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                st[r] = 0.f;
-                dpt[r] = 0.f;
-            }
-            mfma_pipelined<16>(
-                [&](int i) {
-                    const int r = kb * 32 + l32, c = 16 * (i >> 1) + 8 * hf;
-                    return *reinterpret_cast<const u32x4*>((i & 1) ? vt + r * VLD + c : kt + r * KLD + c);
-                },
-                [&](int i, u32x4 op) {
-                    if (i & 1) dpt = mfma32h(as_f16x8(op), df[i >> 1], dpt);
-                    else st = mfma32h(as_f16x8(op), qf[i >> 1], st);
-                });
-            // dS^T * sO = P^T * (dP^T * sO - D * sO), as B operands of two 16-key steps;
-            // key slot (hf, e) of step kk is key kb*32 + 16*kk + 8*(e/4) + 4*hf + e%4
-            f16x8 sb[2];
-            // two copies of the element loop, so that a FULL tile carries no mask test
-            auto form_ds = [&](auto masked_tag) {
-                constexpr bool masked = decltype(masked_tag)::value;
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    u32x4 pk;
-#pragma unroll
-                    for (int e2 = 0; e2 < 8; e2 += 2) {
-                        float v2[2];
-#pragma unroll
-                        for (int j = 0; j < 2; ++j) {
-                            const int r = kk * 8 + e2 + j;
-                            const int kidx = kb * 32 + acc_row(r, hf);
-                            float p = fast_exp2(fmaf(st[r], cS, -lse2));
-                            if constexpr (masked) {
-                                bool vis;
-                                if constexpr (SPARSE) vis = key0 + kidx < T;
-                                else vis = (int)(Mb[w][kidx] << (31 - (pos - p_base))) < 0;
-                                p = vis ? p : 0.f;
-                            }
-                            v2[j] = p * fmaf(dpt[r], inv_sV, -dd);
-                        }
-                        pk[e2 >> 1] = pack_f16(v2[0], v2[1]);
-                    }
-                    sb[kk] = as_f16x8(pk);
+                for (int r = 0; r < 16; ++r) {
+                    st[r] = 0.f;
+                    dpt[r] = 0.f;
                 }
-            };
-            if (need_mask) form_ds(BoolTag<true>{});
-            else form_ds(BoolTag<false>{});
-            mfma_pipelined<8>(
-                [&](int i) {
-                    const int k0 = kb * 32 + 16 * (i & 1) + 4 * hf;
-                    return tr_rows_ld(kt, KLD, k0, k0 + 8, (i >> 1) * 32, lane);
-                },
-                [&](int i, u32x4 op) { acc[i >> 1] = mfma32h(as_f16x8(op), sb[i & 1], acc[i >> 1]); });
+                mfma_pipelined<16>(
+                    [&](int i) {
+                        const int r = kb * 32 + l32, c = 16 * (i >> 1) + 8 * hf;
+                        return *reinterpret_cast<const u32x4*>((i & 1) ? vt + r * VLD + c : kt + r * KLD + c);
+                    },
+                    [&](int i, u32x4 op) {
+                        if (i & 1) dpt = mfma32h(as_f16x8(op), df[i >> 1], dpt);
+                        else st = mfma32h(as_f16x8(op), qf[i >> 1], st);
+                    });
+                // dS^T * sO = P^T * (dP^T * sO - D * sO), as B operands of two 16-key steps;
+                // key slot (hf, e) of step kk is key kb*32 + 16*kk + 8*(e/4) + 4*hf + e%4
+                f16x8 sb[2];
+                // two copies of the element loop, so that a FULL tile carries no mask test
+                auto form_ds = [&](auto masked_tag) {
+                    constexpr bool masked = decltype(masked_tag)::value;
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk) {
+                        u32x4 pk;
+#pragma unroll
+                        for (int e2 = 0; e2 < 8; e2 += 2) {
+                            float v2[2];
+#pragma unroll
+                            for (int j = 0; j < 2; ++j) {
+                                const int r = kk * 8 + e2 + j;
+                                const int kidx = kb * 32 + acc_row(r, hf);
+                                float p = fast_exp2(fmaf(st[r], cS, -lse2));
+                                if constexpr (masked) {
+                                    bool vis;
+                                    if constexpr (SPARSE) vis = key0 + kidx < T;
+                                    else vis = (int)(Mb[w][kidx] << (31 - (pos - p_base))) < 0;
+                                    p = vis ? p : 0.f;
+                                }
+                                v2[j] = p * fmaf(dpt[r], inv_sV, -dd);
+                            }
+                            pk[e2 >> 1] = pack_f16(v2[0], v2[1]);
+                        }
+                        sb[kk] = as_f16x8(pk);
+                    }
+                };
+                if (need_mask) form_ds(BoolTag<true>{});
+                else form_ds(BoolTag<false>{});
+                mfma_pipelined<8>(
+                    [&](int i) {
+                        const int k0 = kb * 32 + 16 * (i & 1) + 4 * hf;
+                        return tr_rows_ld(kt, KLD, k0, k0 + 8, (i >> 1) * 32, lane);
+                    },
+                    [&](int i, u32x4 op) { acc[i >> 1] = mfma32h(as_f16x8(op), sb[i & 1], acc[i >> 1]); });
+            }
         }
         // tile t + 1 into the other slot (its readers of tile t - 1 passed the last
         // barrier), loads of tile t + 2
-        if (t + 1 < ntiles) store_tile(cb ^ 1);
-        if (t + 2 < ntiles) load_tile(t + 2);
+        if (have1) store_tile(cb ^ 1);
+        if (PAIR ? more() : t + 2 < ntiles) load_tile(t + 2);
         lds_barrier();
     }
 
@@ -883,7 +921,7 @@ hipError_t launch_bwd_main(const Problem& P, const void* q, const void* k, const
     if (!P.sparse) {
         hipLaunchKernelGGL((dq_kernel<8, false>), dim3(P.Hk * P.nqt_f), dim3(512), 0, s, b);
     } else if (P.sblock == 64) {
-        hipLaunchKernelGGL((dq_kernel<2, true>), dim3(P.Hk * P.G * P.nb), dim3(128), 0, s, b);
+        hipLaunchKernelGGL((dq_kernel<4, true, true>), dim3(P.Hk * P.G * ((P.nb + 1) / 2)), dim3(256), 0, s, b);
     } else {
         hipLaunchKernelGGL((dq_kernel<4, true>), dim3(P.Hk * P.G * P.nb), dim3(256), 0, s, b);
     }
