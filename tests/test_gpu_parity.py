@@ -108,13 +108,14 @@ def test_block_sparse_mha_and_empty_rows():
     T, Hq, Hk, b = 640, 4, 4, 64
     nb = T // b
     keep = block_sparse_keep(12, Hq, nb, nb)
-    keep[1, 3, :] = 0            # head 1, query block 3: no visible key
+    keep[1, 3, :] = 0            # head 1, query block 3: no visible key (its pair, block 2, has some)
+    keep[3, 4:6, :] = 0          # head 3, query blocks 4 and 5: a pair with no visible key at all
     keep[2, :, 5] = 0            # key block 5 unseen by head 2
     keep[:, :, 9] = 0            # key block 9 unseen by everyone: dK = dV = 0 there
     r, ref = _check(T, Hq, Hk, MaskSpec("block_sparse", sparse_block=b), keep=keep, seed=12)
-    rows = slice(3 * b, 4 * b)
-    assert np.all(r["o"][rows, 1] == 0) and np.all(np.isneginf(r["lse"][1, rows]))
-    assert np.all(r["dq"][rows, 1] == 0)
+    for h, rows in ((1, slice(3 * b, 4 * b)), (3, slice(4 * b, 6 * b))):
+        assert np.all(r["o"][rows, h] == 0) and np.all(np.isneginf(r["lse"][h, rows]))
+        assert np.all(r["dq"][rows, h] == 0)
     assert np.all(r["dk"][9 * b:10 * b] == 0) and np.all(r["dv"][9 * b:10 * b] == 0)
 
 
