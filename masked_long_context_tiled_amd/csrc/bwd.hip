@@ -241,14 +241,19 @@ __device__ __forceinline__ RowMap row_map(const BwdArgs& a, int g, int e) {
 // products run on fp16 operands (the preprocess's scaled copies of Q, K, V, dO).
 //
 // The roles run one step apart, so a step (32 query rows) needs a single barrier:
-//   step s, A: S and P of step s + 1 (P -> LDS slot (s+1)%2 and registers),
-//              dV^T += dO_s^T P_s (P_s kept in registers from step s - 1),
+//   step s, A: dV^T += dO_s^T P_s (P_s kept in registers from step s - 1),
+//              S and P of step s + 1 (P -> LDS slot (s+1)%2 and registers),
 //              stage Q, LSE of step s + 2 into Q slot (s+2)%3, load step s + 3;
-//   step s, B: dP_s = dO_s V^T, dS_s = P_s * (dP_s - D_s) with P_s from LDS slot s%2,
-//              dK^T += Q_s^T dS_s, stage dO, D of step s + 1 into slot (s+1)%2, load s + 2.
-// Q_j is read in steps j - 1 (A) and j (B) and written in step j - 2, hence three slots;
-// dO_j and P_j are read in step j only and written in step j - 1, hence two. Every slot
-// is rewritten only after the barrier that ends the last step reading its old content.
+//   step s, B: dS_s = P_s * (dP_s - D_s) with P_s from LDS slot s%2 and dP_s kept in
+//              registers from step s - 1, dK^T += Q_s^T dS_s, then dP_{s+1} = dO_{s+1} V^T,
+//              stage dO, D of step s + 2 into slot (s+2)%3, load step s + 3.
+// Each wave thus alternates a vector phase with a run of 16 MFMAs, in opposite order to its
+// partner on the SIMD: B forms dS while A issues its dV and S MFMAs, and A forms P while B
+// issues its dK and dP MFMAs.
+// Q_j is read in steps j - 1 (A) and j (B), dO_j in steps j - 1 (B) and j (A), and both are
+// written in step j - 2, hence three slots each; P_j is read in step j and written in step
+// j - 1, hence two. Every slot is rewritten only after the barrier that ends the last step
+// reading its old content.
 template <int NWK, bool SPARSE>
 __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
     constexpr int NR = NWK * 64;          // threads per role
@@ -260,7 +265,7 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
     constexpr bool SKEW = NWK == 4;
     constexpr int PITCH = SKEW ? SKEW_PITCH : HEAD_DIM;
     __shared__ __attribute__((aligned(16))) _Float16 Qh[3][32 * PITCH];
-    __shared__ __attribute__((aligned(16))) _Float16 dOh[2][32 * PITCH];
+    __shared__ __attribute__((aligned(16))) _Float16 dOh[3][32 * PITCH];
     auto roff = [](int q, int col) { return SKEW ? skew_off(q, col) : swz_off(q, col); };
     auto rtr = [](const _Float16* M, int rb16, int c0, int ln) {
         if constexpr (SKEW) return tr_rows_skew(M, rb16, c0, ln);
@@ -268,7 +273,7 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
     };
     __shared__ __attribute__((aligned(16))) _Float16 Ps[2][NWK * 2 * 64 * 8]; // [kb][kk][lane][8]
     __shared__ __attribute__((aligned(16))) float lse_s[3][32];
-    __shared__ __attribute__((aligned(16))) float dd_s[2][32];
+    __shared__ __attribute__((aligned(16))) float dd_s[3][32];
 
     const int tid = threadIdx.x, lane = tid & 63;
     // wave index made uniform (SGPR), so the role branches are scalar branches
@@ -441,40 +446,50 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
-    // prologue: A stages Q_0 and Q_1, B stages dO_0; A forms P_0; loads of Q_2 / dO_1
+    // B: dP = (dO * sO) V^T of the rows in dO slot os (scaled by sO * sV)
+    auto dp_of = [&](int os) {
+        f32x16 d;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) d[r] = 0.f;
+        const _Float16* doh = dOh[os];
+        mfma_pipelined<8>(
+            [&](int ks) { return *reinterpret_cast<const u32x4*>(&doh[roff(l32, 16 * ks + 8 * hf)]); },
+            [&](int ks, u32x4 op) { d = mfma32h(as_f16x8(op), kvf[ks], d); });
+        return d;
+    };
+
+    // prologue: A stages Q_0 and Q_1, B stages dO_0 and dO_1; then A forms P_0 and B dP_0,
+    // and both load the rows of step 2
     if (nsteps > 0) {
-        if (is_a) {
-            load_rows(0);
-            store_rows(0);
-            if (nsteps > 1) {
-                load_rows(1);
-                store_rows(1);
-            }
-        } else {
-            load_rows(0);
-            store_rows(0);
+        load_rows(0);
+        store_rows(0);
+        if (nsteps > 1) {
+            load_rows(1);
+            store_rows(1);
         }
     }
     lds_barrier();
     f16x8 pb_cur[2];   // A: P of the step being finished
-    if (nsteps > 0 && is_a) {
+    f32x16 dpacc;      // B: dP of the step being finished
+    if (nsteps > 0) {
         // settle the one-time loads here, so no step waits for them behind its prefetches
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        s_and_p(0, nsteps > 1 ? e_q0 : e_q1, 0, pb_cur);   // loads so far: steps 0 and 1
+        if (is_a) s_and_p(0, nsteps > 1 ? e_q0 : e_q1, 0, pb_cur);   // loads so far: steps 0 and 1
+        else dpacc = dp_of(0);
         if (nsteps > 2) load_rows(2);
     }
-    if (nsteps > 1 && !is_a) load_rows(1);
     lds_barrier();
 
     if (is_a) {
         // At the top of step s the last two loads were of steps s + 1 and s + 2 (e_q0, e_q1),
         // or of steps s and s + 1 when s + 2 is past the end.
         int qs1 = 1;   // Q slot of step s + 1
+        int os = 0;    // dO slot of step s
         for (int step = 0; step < nsteps; ++step) {
             // dV^T += (dO * sO)^T P of this step first (P from the previous step), then S and
             // P of the next step: the exponentials then run while the B wave on the same SIMD
-            // issues its dK MFMAs, and B's dS work while this wave issues MFMAs
-            const _Float16* doh = dOh[step & 1];
+            // issues its dK and dP MFMAs, and B's dS work while this wave issues MFMAs
+            const _Float16* doh = dOh[os];
             mfma_pipelined<8>(
                 [&](int i) { return rtr(doh, 16 * (i & 1), (i >> 1) * 32, lane); },
                 [&](int i, u32x4 op) { acc[i >> 1] = mfma32h(as_f16x8(op), pb_cur[i & 1], acc[i >> 1]); });
@@ -484,29 +499,21 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
             if (step + 2 < nsteps) store_rows(qs2);
             if (step + 3 < nsteps) load_rows(step + 3);
             qs1 = qs2;
+            os = os == 2 ? 0 : os + 1;
             lds_barrier();
         }
     } else {
-        int qs0 = 0;   // Q slot of step s
+        int qs0 = 0;   // Q and dO slot of step s
         for (int step = 0; step < nsteps; ++step) {
             const int cb = step & 1;
-            // dP = dO V^T (scaled by sO * sV)
-            f32x16 dpacc;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) dpacc[r] = 0.f;
-            const _Float16* doh = dOh[cb];
-            mfma_pipelined<8>(
-                [&](int ks) { return *reinterpret_cast<const u32x4*>(&doh[roff(l32, 16 * ks + 8 * hf)]); },
-                [&](int ks, u32x4 op) { dpacc = mfma32h(as_f16x8(op), kvf[ks], dpacc); });
-
             // dS * sO = P * (dP * sO - D * sO); dK^T += (Q * sQ)^T (dS * sO)
             f16x8 sb[2];
             const _Float16* ps = Ps[cb];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 const f16x8 ph = as_f16x8(*reinterpret_cast<const u32x4*>(&ps[((kb * 2 + kk) * 64 + lane) * 8]));
-                const float4 d0v = *reinterpret_cast<const float4*>(&dd_s[cb][16 * kk + 4 * hf]);
-                const float4 d1v = *reinterpret_cast<const float4*>(&dd_s[cb][16 * kk + 8 + 4 * hf]);
+                const float4 d0v = *reinterpret_cast<const float4*>(&dd_s[qs0][16 * kk + 4 * hf]);
+                const float4 d1v = *reinterpret_cast<const float4*>(&dd_s[qs0][16 * kk + 8 + 4 * hf]);
                 const float dr[8] = {d0v.x, d0v.y, d0v.z, d0v.w, d1v.x, d1v.y, d1v.z, d1v.w};
                 // (dP - D) in fp32, rounded to fp16, times P in packed fp16
                 f16x8 sk;
@@ -528,9 +535,12 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
             mfma_pipelined<8>(
                 [&](int i) { return rtr(qh, 16 * (i & 1), (i >> 1) * 32, lane); },
                 [&](int i, u32x4 op) { acc[i >> 1] = mfma32h(as_f16x8(op), sb[i & 1], acc[i >> 1]); });
-            if (step + 1 < nsteps) store_rows(cb ^ 1);
-            if (step + 2 < nsteps) load_rows(step + 2);
-            qs0 = qs0 == 2 ? 0 : qs0 + 1;
+            const int qs1 = qs0 == 2 ? 0 : qs0 + 1, qs2 = qs1 == 2 ? 0 : qs1 + 1;
+            // dP of the next step (its dO rows were staged a step earlier)
+            if (step + 1 < nsteps) dpacc = dp_of(qs1);
+            if (step + 2 < nsteps) store_rows(qs2);
+            if (step + 3 < nsteps) load_rows(step + 3);
+            qs0 = qs1;
             lds_barrier();
         }
     }
