@@ -23,23 +23,38 @@ from .masks import mask_block
 EMPTY, PARTIAL, FULL = 0, 1, 2
 
 
-def tile_classes(spec, T, BM, BN, h=0, keep=None):
-    """uint8 [ceil(T/BM)][ceil(T/BN)] class map from the materialised mask."""
+def tile_classes(spec, T, BM, BN, h=0, keep=None, rows_per_pass=None):
+    """uint8 [ceil(T/BM)][ceil(T/BN)] class map from the materialised mask.
+
+    The mask is materialised a few query tiles at a time (``rows_per_pass`` rows, a
+    multiple of BM, by default enough for about 2^24 cells) and every tile is read in
+    full: any visible cell makes it non-EMPTY, every in-range cell visible makes it FULL.
+    Cells past T (the ragged last key tile) count as neither."""
     nqt = -(-T // BM)
     nkt = -(-T // BN)
     cls = np.empty((nqt, nkt), dtype=np.uint8)
     cols = np.arange(T)
-    for qt in range(nqt):
-        rows = np.arange(qt * BM, min(T, (qt + 1) * BM))
-        M = mask_block(spec, T, rows, cols, h, keep)
-        for kt in range(nkt):
-            blk = M[:, kt * BN:min(T, (kt + 1) * BN)]
-            if not blk.any():
-                cls[qt, kt] = EMPTY
-            elif blk.all():
-                cls[qt, kt] = FULL
-            else:
-                cls[qt, kt] = PARTIAL
+    if rows_per_pass is None:
+        rows_per_pass = max(BM, (1 << 24) // max(1, nkt * BN) // BM * BM)
+    in_range = np.zeros(nkt * BN, dtype=bool)
+    in_range[:T] = True
+    for r0 in range(0, nqt * BM, rows_per_pass):
+        r1 = min(T, r0 + rows_per_pass)
+        rows = np.arange(r0, r1)
+        vis = np.zeros((len(rows), nkt * BN), dtype=bool)
+        vis[:, :T] = mask_block(spec, T, rows, cols, h, keep)
+        nq = -(-len(rows) // BM)
+        pad = nq * BM - len(rows)          # rows past T: neither visible nor required
+        if pad:
+            vis = np.concatenate([vis, np.zeros((pad, nkt * BN), dtype=bool)])
+        row_in = np.zeros(nq * BM, dtype=bool)
+        row_in[:len(rows)] = True
+        cell_in = row_in[:, None] & in_range[None, :]
+        shape = (nq, BM, nkt, BN)
+        any_vis = vis.reshape(shape).any(axis=(1, 3))
+        all_vis = (vis | ~cell_in).reshape(shape).all(axis=(1, 3))
+        q0 = r0 // BM
+        cls[q0:q0 + nq] = np.where(all_vis, FULL, np.where(any_vis, PARTIAL, EMPTY))
     return cls
 
 
@@ -75,3 +90,10 @@ def keep_csr(keep_2d):
 def keep_csc(keep_2d):
     """(col_ptr, rows) of a 2-D keep matrix, ascending."""
     return keep_csr(np.ascontiguousarray(keep_2d.T))
+
+
+def launch_order(ptr):
+    """Launch order of a list set: list indices by descending length (ptr[i+1] - ptr[i]),
+    equal lengths by ascending index."""
+    lens = np.diff(np.asarray(ptr, dtype=np.int64))
+    return np.asarray(sorted(range(len(lens)), key=lambda i: (-int(lens[i]), i)), dtype=np.int32)
