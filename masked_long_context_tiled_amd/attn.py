@@ -19,7 +19,9 @@ import numpy as np
 from .inputs import MASK_KINDS, VARIABLE_BLOCK, MaskSpec
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libattn.so")
+# MLCT_ATTN_LIB names another build of the same library (the CPU tests point it at the
+# host-only sanitizer build, whose kernel launchers abort); by default the in-tree build.
+LIB_PATH = os.environ.get("MLCT_ATTN_LIB") or os.path.join(_HERE, "libattn.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "attn.h")
 
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_WORKSPACE, ATTN_ERR_HIP = range(5)

@@ -854,8 +854,9 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
     }
 }
 
-hipError_t launch_bwd_pre(const Problem& P, const void* q, const void* k, const void* v, const void* o,
-                          const void* o_lo, const void* dout, float* dbuf, hipStream_t s) {
+int launch_bwd_pre(const Problem& P, const void* q, const void* k, const void* v, const void* o,
+                   const void* o_lo, const void* dout, float* dbuf, void* stream) {
+    const hipStream_t s = static_cast<hipStream_t>(stream);
     const BwdLayout W = bwd_layout(P.Hq, P.Hk, P.T);
     char* ws = reinterpret_cast<char*>(dbuf);
     float* stats = reinterpret_cast<float*>(ws + W.stats);
@@ -870,12 +871,13 @@ hipError_t launch_bwd_pre(const Problem& P, const void* q, const void* k, const 
                        static_cast<const u32x4*>(dout), static_cast<const u32x4*>(k), static_cast<const u32x4*>(v),
                        reinterpret_cast<u32x4*>(ws + W.qh), reinterpret_cast<u32x4*>(ws + W.doh),
                        reinterpret_cast<u32x4*>(ws + W.kh), reinterpret_cast<u32x4*>(ws + W.vh), nq8, nk8, stats);
-    return hipGetLastError();
+    return (int)hipGetLastError();
 }
 
-hipError_t launch_bwd_main(const Problem& P, const void* q, const void* k, const void* v, const float* lse,
-                           const void* dout, float* dq, float* dk, float* dv, const int4* desc,
-                           const void* index, const float* dbuf, int parts, hipStream_t s) {
+int launch_bwd_main(const Problem& P, const void* q, const void* k, const void* v, const float* lse,
+                    const void* dout, float* dq, float* dk, float* dv, const int32_t* desc, const void* index,
+                    const float* dbuf, int parts, void* stream) {
+    const hipStream_t s = static_cast<hipStream_t>(stream);
     const IndexLayout L = index_layout(P);
     const char* base = static_cast<const char*>(index);
     BwdArgs a;
@@ -895,7 +897,7 @@ hipError_t launch_bwd_main(const Problem& P, const void* q, const void* k, const
     a.dq = dq;
     a.dk = dk;
     a.dv = dv;
-    a.desc = desc;
+    a.desc = reinterpret_cast<const int4*>(desc);
     a.ptr = reinterpret_cast<const int*>(base + L.bwd_ptr);
     a.ent = reinterpret_cast<const int*>(base + L.bwd_ent);
     a.order = P.sparse ? nullptr : reinterpret_cast<const int*>(base + L.bwd_order);
@@ -918,9 +920,9 @@ hipError_t launch_bwd_main(const Problem& P, const void* q, const void* k, const
             hipLaunchKernelGGL((bwd_kernel<4, true>), dim3(P.Hk * P.nb), dim3(512), 0, s, a);
         }
         hipError_t err = hipGetLastError();
-        if (err != hipSuccess) return err;
+        if (err != hipSuccess) return (int)err;
     }
-    if (!(parts & BWD_PART_DQ)) return hipSuccess;
+    if (!(parts & BWD_PART_DQ)) return 0;
 
     // dQ pass on the forward's lists
     BwdArgs b = a;
@@ -935,12 +937,13 @@ hipError_t launch_bwd_main(const Problem& P, const void* q, const void* k, const
     } else {
         hipLaunchKernelGGL((dq_kernel<4, true>), dim3(P.Hk * P.G * P.nb), dim3(256), 0, s, b);
     }
-    return hipGetLastError();
+    return (int)hipGetLastError();
 }
 
-hipError_t launch_cast_bf16(const float* in, void* out, size_t n, hipStream_t s) {
-    hipLaunchKernelGGL(cast_kernel, dim3(2048), dim3(256), 0, s, in, static_cast<uint16_t*>(out), n);
-    return hipGetLastError();
+int launch_cast_bf16(const float* in, void* out, size_t n, void* stream) {
+    hipLaunchKernelGGL(cast_kernel, dim3(2048), dim3(256), 0, static_cast<hipStream_t>(stream), in,
+                       static_cast<uint16_t*>(out), n);
+    return (int)hipGetLastError();
 }
 
 }  // namespace mlct

@@ -5,14 +5,10 @@
 #include <stdint.h>
 #include <stddef.h>
 
-#include "../../include/attn.h"
+#include "host.h"
 
 namespace mlct {
 
-constexpr int HEAD_DIM = 128;
-constexpr int FWD_BN = 64;          // keys per forward tile
-constexpr int BWD_BN = 128;         // keys per dense backward tile (4 waves x 32 keys)
-constexpr int ROWS_PER_WG = 256;    // (head, position) rows per dense forward work item
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
@@ -205,70 +201,5 @@ __device__ __forceinline__ u32x4 tr_rows_skew(const void* Mv, int rb16, int c0, 
     const u32x2 hi = ds_read_tr16(p + 8 * SKEW_PITCH + 16);
     return u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
-
-// Round an offset up to 256 bytes.
-__host__ __device__ constexpr size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
-
-// Host-side description of one problem after validation.
-struct Problem {
-    int T, Hq, Hk, G;
-    int kind;
-    int sblock;         // block-sparse block edge (0 otherwise)
-    float scale;
-    bool sparse;
-    // dense tiles
-    int fBM, fBN, bBM, bBN;
-    int lgBM;           // log2(fBM) = log2(bBM)
-    int nqt_f, nkt_f, nqt_b, nkt_b;
-    // block-sparse
-    int nb;
-};
-
-// Backward workspace, in order (each part 256-byte aligned):
-//   D [Hq][T] fp32 | BWD_STATS fp32 bounds of the operands | Q, dO [T][Hq][128] and
-//   K, V [T][Hk][128] as fp16 multiplied by their power-of-two scales (see bwd.hip).
-constexpr int BWD_STATS = 4;
-struct BwdLayout {
-    size_t stats, qh, doh, kh, vh, total;
-};
-__host__ __device__ inline BwdLayout bwd_layout(int Hq, int Hk, int T) {
-    BwdLayout L;
-    const size_t qbytes = align256((size_t)T * Hq * 128 * 2), kbytes = align256((size_t)T * Hk * 128 * 2);
-    L.stats = align256((size_t)Hq * T * 4);
-    L.qh = L.stats + 256;
-    L.doh = L.qh + qbytes;
-    L.kh = L.doh + qbytes;
-    L.vh = L.kh + kbytes;
-    L.total = L.vh + kbytes;
-    return L;
-}
-
-struct IndexLayout {
-    size_t fwd_cls, fwd_ptr, fwd_ent, fwd_order;
-    size_t bwd_cls, bwd_ptr, bwd_ent, bwd_order;
-    size_t total;
-};
-
-attn_status validate_problem(const attn_problem* p, Problem* out);
-IndexLayout index_layout(const Problem& P);
-
-// Kernel launchers (defined next to their kernels).
-hipError_t launch_index_dense(const Problem& P, const int4* desc, void* index, hipStream_t s);
-hipError_t launch_index_sparse(const Problem& P, const uint8_t* keep, void* index, hipStream_t s);
-hipError_t launch_fwd(const Problem& P, const void* q, const void* k, const void* v, void* o, void* o_lo,
-                      float* lse, const int4* desc, const void* index, hipStream_t s);
-hipError_t launch_bwd_pre(const Problem& P, const void* q, const void* k, const void* v, const void* o,
-                          const void* o_lo, const void* dout, float* dbuf, hipStream_t s);
-enum { BWD_PART_DKDV = 1, BWD_PART_DQ = 2 };
-hipError_t launch_bwd_main(const Problem& P, const void* q, const void* k, const void* v, const float* lse,
-                           const void* dout, float* dq, float* dk, float* dv, const int4* desc,
-                           const void* index, const float* dbuf, int parts, hipStream_t s);
-hipError_t launch_cast_bf16(const float* in, void* out, size_t n, hipStream_t s);
-constexpr int SEL_MAX_NB = 4096;   // longest row of blocks the selection kernel sorts
-size_t select_workspace_bytes(const Problem& P);
-hipError_t launch_block_select(const Problem& P, int mode, int topk, float topp, int keep_diag, const void* q,
-                               const void* k, float* scores, uint8_t* keep, void* ws, hipStream_t s);
-hipError_t launch_lse_merge(const Problem& P, void* o, void* o_lo, float* lse, const void* o_part,
-                            const void* o_part_lo, const float* lse_part, hipStream_t s);
 
 }  // namespace mlct

@@ -542,8 +542,9 @@ __global__ __launch_bounds__(512) void fwd_dense_kernel(FwdArgs a) {
     }
 }
 
-hipError_t launch_fwd(const Problem& P, const void* q, const void* k, const void* v, void* o, void* o_lo,
-                      float* lse, const int4* desc, const void* index, hipStream_t s) {
+int launch_fwd(const Problem& P, const void* q, const void* k, const void* v, void* o, void* o_lo, float* lse,
+               const int32_t* desc, const void* index, void* stream) {
+    const hipStream_t s = static_cast<hipStream_t>(stream);
     const IndexLayout L = index_layout(P);
     const char* base = static_cast<const char*>(index);
     FwdArgs a;
@@ -553,7 +554,7 @@ hipError_t launch_fwd(const Problem& P, const void* q, const void* k, const void
     a.o = static_cast<bf16*>(o);
     a.o_lo = static_cast<bf16*>(o_lo);
     a.lse = lse;
-    a.desc = desc;
+    a.desc = reinterpret_cast<const int4*>(desc);
     a.ptr = reinterpret_cast<const int*>(base + L.fwd_ptr);
     a.ent = reinterpret_cast<const int*>(base + L.fwd_ent);
     a.order = P.sparse ? nullptr : reinterpret_cast<const int*>(base + L.fwd_order);
@@ -573,7 +574,7 @@ hipError_t launch_fwd(const Problem& P, const void* q, const void* k, const void
     } else {
         hipLaunchKernelGGL((fwd_sparse_kernel<4>), dim3(P.Hk * P.G * P.nb), dim3(256), 0, s, a);
     }
-    return hipGetLastError();
+    return (int)hipGetLastError();
 }
 
 }  // namespace mlct

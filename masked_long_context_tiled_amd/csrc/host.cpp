@@ -1,9 +1,11 @@
 // C-ABI entry points: argument validation, the host column-interval descriptor builder,
-// the tile-index layout and the launches. No allocation, no global state.
+// the Variable Block expansion, the tile-index layout and the calls of the kernel
+// launchers. Plain C++ (no HIP types): the launchers are declared in host.h and defined
+// next to their kernels. No allocation, no global state.
 #include <math.h>
 #include <string.h>
 
-#include "common.h"
+#include "host.h"
 
 namespace mlct {
 
@@ -221,7 +223,7 @@ static attn_status validate_mask(const attn_mask_params* mp, int32_t T) {
     }
 }
 
-static attn_status hip_status(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
+static attn_status hip_status(int e) { return e == 0 ? ATTN_OK : ATTN_ERR_HIP; }
 
 }  // namespace mlct
 
@@ -265,7 +267,7 @@ attn_status attn_lse_merge(const attn_problem* prob, void* o, void* o_lo, float*
     attn_status st = validate_problem(prob, &P);
     if (st != ATTN_OK) return st;
     if (!o || !lse || !o_part || !lse_part) return ATTN_ERR_INVALID_ARG;
-    return hip_status(launch_lse_merge(P, o, o_lo, lse, o_part, o_part_lo, lse_part, (hipStream_t)stream));
+    return hip_status(launch_lse_merge(P, o, o_lo, lse, o_part, o_part_lo, lse_part, stream));
 }
 
 attn_status attn_block_select_workspace_size(const attn_problem* prob, size_t* bytes_out) {
@@ -277,13 +279,11 @@ attn_status attn_block_select_workspace_size(const attn_problem* prob, size_t* b
     return ATTN_OK;
 }
 
-attn_status attn_block_select(const attn_problem* prob, const attn_block_select_params* sp, const void* q,
-                              const void* k, float* scores, uint8_t* keep_out, void* ws, size_t ws_bytes,
-                              void* stream) {
-    Problem P;
-    attn_status st = validate_problem(prob, &P);
+static attn_status validate_select(const attn_problem* prob, const attn_block_select_params* sp, const void* q,
+                                   const void* k, const float* scores, const uint8_t* keep_out, Problem* P) {
+    attn_status st = validate_problem(prob, P);
     if (st != ATTN_OK) return st;
-    if (!P.sparse || !sp || !q || !k || !scores || !keep_out || !ws) return ATTN_ERR_INVALID_ARG;
+    if (!P->sparse || !sp || !q || !k || !scores || !keep_out) return ATTN_ERR_INVALID_ARG;
     if (sp->mode == ATTN_SELECT_TOPK) {
         if (sp->topk < 1) return ATTN_ERR_INVALID_ARG;
     } else if (sp->mode == ATTN_SELECT_TOPP) {
@@ -291,11 +291,21 @@ attn_status attn_block_select(const attn_problem* prob, const attn_block_select_
     } else {
         return ATTN_ERR_INVALID_ARG;
     }
-    if (P.nb > SEL_MAX_NB) return ATTN_ERR_UNSUPPORTED;
+    if (P->nb > SEL_MAX_NB) return ATTN_ERR_UNSUPPORTED;
+    return ATTN_OK;
+}
+
+attn_status attn_block_select(const attn_problem* prob, const attn_block_select_params* sp, const void* q,
+                              const void* k, float* scores, uint8_t* keep_out, void* ws, size_t ws_bytes,
+                              void* stream) {
+    Problem P;
+    attn_status st = validate_select(prob, sp, q, k, scores, keep_out, &P);
+    if (st != ATTN_OK) return st;
+    if (!ws) return ATTN_ERR_INVALID_ARG;
     if (ws_bytes < select_workspace_bytes(P)) return ATTN_ERR_WORKSPACE;
     return hip_status(launch_block_select(P, sp->mode, sp->topk < P.nb ? sp->topk : P.nb, sp->topp,
                                           sp->keep_diagonal ? 1 : 0, q, k, scores, keep_out, ws,
-                                          (hipStream_t)stream));
+                                          stream));
 }
 
 // Block edges 0 = off[0] < off[1] < ... < off[n] = T, the interior ones multiples of 64.
@@ -390,8 +400,8 @@ attn_status attn_tile_index_build(const attn_problem* prob, const int32_t* desc_
     if (st != ATTN_OK) return st;
     if (P.sparse || !desc_dev || !index_dev) return ATTN_ERR_INVALID_ARG;
     if (index_bytes < index_layout(P).total) return ATTN_ERR_WORKSPACE;
-    return hip_status(launch_index_dense(P, reinterpret_cast<const int4*>(desc_dev), index_dev,
-                                         (hipStream_t)stream));
+    return hip_status(launch_index_dense(P, desc_dev, index_dev,
+                                         stream));
 }
 
 attn_status attn_block_index_build(const attn_problem* prob, const uint8_t* keep_dev, void* index_dev,
@@ -401,7 +411,7 @@ attn_status attn_block_index_build(const attn_problem* prob, const uint8_t* keep
     if (st != ATTN_OK) return st;
     if (!P.sparse || !keep_dev || !index_dev) return ATTN_ERR_INVALID_ARG;
     if (index_bytes < index_layout(P).total) return ATTN_ERR_WORKSPACE;
-    return hip_status(launch_index_sparse(P, keep_dev, index_dev, (hipStream_t)stream));
+    return hip_status(launch_index_sparse(P, keep_dev, index_dev, stream));
 }
 
 attn_status attn_fwd_workspace_size(const attn_problem* prob, size_t* bytes_out) {
@@ -432,8 +442,8 @@ attn_status attn_fwd(const attn_problem* prob, const void* q, const void* k, con
     if (!q || !k || !v || !o || !lse || !index_dev) return ATTN_ERR_INVALID_ARG;
     if (!P.sparse && !desc_dev) return ATTN_ERR_INVALID_ARG;
     if (index_bytes < index_layout(P).total) return ATTN_ERR_WORKSPACE;
-    return hip_status(launch_fwd(P, q, k, v, o, o_lo, lse, reinterpret_cast<const int4*>(desc_dev), index_dev,
-                                 (hipStream_t)stream));
+    return hip_status(launch_fwd(P, q, k, v, o, o_lo, lse, desc_dev, index_dev,
+                                 stream));
 }
 
 static attn_status check_bwd_ws(const attn_problem* prob, const void* ws, size_t ws_bytes) {
@@ -450,7 +460,7 @@ attn_status attn_bwd_preprocess(const attn_problem* prob, const void* q, const v
     if (st != ATTN_OK) return st;
     if (!q || !k || !v || !o || !dout) return ATTN_ERR_INVALID_ARG;
     if ((st = check_bwd_ws(prob, ws, ws_bytes)) != ATTN_OK) return st;
-    return hip_status(launch_bwd_pre(P, q, k, v, o, o_lo, dout, (float*)ws, (hipStream_t)stream));
+    return hip_status(launch_bwd_pre(P, q, k, v, o, o_lo, dout, (float*)ws, stream));
 }
 
 static attn_status bwd_parts(const attn_problem* prob, const void* q, const void* k, const void* v,
@@ -465,8 +475,8 @@ static attn_status bwd_parts(const attn_problem* prob, const void* q, const void
     if (!P.sparse && !desc_dev) return ATTN_ERR_INVALID_ARG;
     if (index_bytes < index_layout(P).total) return ATTN_ERR_WORKSPACE;
     if ((st = check_bwd_ws(prob, ws, ws_bytes)) != ATTN_OK) return st;
-    return hip_status(launch_bwd_main(P, q, k, v, lse, dout, dq, dk, dv, reinterpret_cast<const int4*>(desc_dev),
-                                      index_dev, (const float*)ws, parts, (hipStream_t)stream));
+    return hip_status(launch_bwd_main(P, q, k, v, lse, dout, dq, dk, dv, desc_dev,
+                                      index_dev, (const float*)ws, parts, stream));
 }
 
 attn_status attn_bwd_main(const attn_problem* prob, const void* q, const void* k, const void* v,
@@ -514,7 +524,7 @@ attn_status attn_bwd(const attn_problem* prob, const void* q, const void* k, con
 attn_status attn_cast_bf16(const float* in, void* out, size_t n, void* stream) {
     if (n == 0) return ATTN_OK;
     if (!in || !out) return ATTN_ERR_INVALID_ARG;
-    return hip_status(launch_cast_bf16(in, out, n, (hipStream_t)stream));
+    return hip_status(launch_cast_bf16(in, out, n, stream));
 }
 
 }  // extern "C"

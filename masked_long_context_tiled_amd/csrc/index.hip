@@ -179,7 +179,9 @@ static hipError_t run_lists(const ListJob& a, const ListJob& b, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_index_dense(const Problem& P, const int4* desc, void* index, hipStream_t s) {
+int launch_index_dense(const Problem& P, const int32_t* desc_words, void* index, void* stream) {
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const int4* desc = reinterpret_cast<const int4*>(desc_words);
     const IndexLayout L = index_layout(P);
     char* base = static_cast<char*>(index);
     uint8_t* fcls = reinterpret_cast<uint8_t*>(base + L.fwd_cls);
@@ -196,19 +198,20 @@ hipError_t launch_index_dense(const Problem& P, const int4* desc, void* index, h
     const ClassifyJob cb{P.bBM, P.bBN, P.nqt_b, P.nkt_b, bcls, (int)((nbk + 255) / 256)};
     hipLaunchKernelGGL(classify_kernel, dim3((unsigned)(cf.blocks + cb.blocks)), dim3(256), 0, s, desc, P.T, cf, cb);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess) return (int)e;
     // forward: rows of the class map (one list per query tile); backward: its columns (one
     // list per key tile)
     const ListJob lf = list_job(fcls, ListGeom{P.nqt_f, P.nkt_f, 1, P.nkt_f, 0, 1}, fptr, fent, 1);
     const ListJob lb = list_job(bcls, ListGeom{P.nkt_b, P.nqt_b, 1, 1, 0, P.nkt_b}, bptr, bent, 1);
-    if ((e = run_lists(lf, lb, s)) != hipSuccess) return e;
+    if ((e = run_lists(lf, lb, s)) != hipSuccess) return (int)e;
     const OrderJob of{fptr, P.nqt_f, ford, (P.nqt_f + 255) / 256};
     const OrderJob ob{bptr, P.nkt_b, bord, (P.nkt_b + 255) / 256};
     hipLaunchKernelGGL(order_kernel, dim3((unsigned)(of.blocks + ob.blocks)), dim3(256), 0, s, of, ob);
-    return hipGetLastError();
+    return (int)hipGetLastError();
 }
 
-hipError_t launch_index_sparse(const Problem& P, const uint8_t* keep, void* index, hipStream_t s) {
+int launch_index_sparse(const Problem& P, const uint8_t* keep, void* index, void* stream) {
+    const hipStream_t s = static_cast<hipStream_t>(stream);
     const IndexLayout L = index_layout(P);
     char* base = static_cast<char*>(index);
     int* fptr = reinterpret_cast<int*>(base + L.fwd_ptr);
@@ -220,7 +223,7 @@ hipError_t launch_index_sparse(const Problem& P, const uint8_t* keep, void* inde
     // columns (g, kb): elements m = hi * nb + qb at keep[((g*G + hi) * nb + qb) * nb + kb]
     const ListJob lf = list_job(keep, ListGeom{P.Hq * nb, nb, 1, nb, 0, 1}, fptr, fent, 0);
     const ListJob lb = list_job(keep, ListGeom{P.Hk * nb, P.G * nb, nb, (long)P.G * nb * nb, 1, nb}, bptr, bent, 0);
-    return run_lists(lf, lb, s);
+    return (int)run_lists(lf, lb, s);
 }
 
 }  // namespace mlct

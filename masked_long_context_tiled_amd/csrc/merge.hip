@@ -51,13 +51,14 @@ __global__ __launch_bounds__(256) void lse_merge_kernel(bf16* __restrict__ o, bf
     if (part == 0) lse[li] = lout;
 }
 
-hipError_t launch_lse_merge(const Problem& P, void* o, void* o_lo, float* lse, const void* o_part,
-                            const void* o_part_lo, const float* lse_part, hipStream_t s) {
+int launch_lse_merge(const Problem& P, void* o, void* o_lo, float* lse, const void* o_part,
+                     const void* o_part_lo, const float* lse_part, void* stream) {
+    const hipStream_t s = static_cast<hipStream_t>(stream);
     const long rows = (long)P.T * P.Hq;
     hipLaunchKernelGGL(lse_merge_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, s,
                        static_cast<bf16*>(o), static_cast<bf16*>(o_lo), lse, static_cast<const bf16*>(o_part),
                        static_cast<const bf16*>(o_part_lo), lse_part, P.T, P.Hq);
-    return hipGetLastError();
+    return (int)hipGetLastError();
 }
 
 }  // namespace mlct

@@ -203,14 +203,11 @@ __global__ __launch_bounds__(256) void block_select_kernel(const float* __restri
     }
 }
 
-size_t select_workspace_bytes(const Problem& P) {
-    return align256((size_t)P.Hq * P.nb * HEAD_DIM * 4) + align256((size_t)P.Hk * P.nb * HEAD_DIM * 4);
-}
-
-hipError_t launch_block_select(const Problem& P, int mode, int topk, float topp, int keep_diag, const void* q,
-                               const void* k, float* scores, uint8_t* keep, void* ws, hipStream_t s) {
+int launch_block_select(const Problem& P, int mode, int topk, float topp, int keep_diag, const void* q,
+                        const void* k, float* scores, uint8_t* keep, void* ws, void* stream) {
+    const hipStream_t s = static_cast<hipStream_t>(stream);
     float* qbar = static_cast<float*>(ws);
-    float* kbar = reinterpret_cast<float*>(static_cast<char*>(ws) + align256((size_t)P.Hq * P.nb * HEAD_DIM * 4));
+    float* kbar = reinterpret_cast<float*>(static_cast<char*>(ws) + select_qbar_bytes(P));
     const int b = P.sblock, nb = P.nb;
     hipLaunchKernelGGL(pool_kernel, dim3(nb, (P.Hq + 15) / 16), dim3(256), 0, s, static_cast<const bf16*>(q), P.T,
                        P.Hq, b, nb, qbar);
@@ -222,7 +219,7 @@ hipError_t launch_block_select(const Problem& P, int mode, int topk, float topp,
     while (Pp < nb) Pp <<= 1;
     hipLaunchKernelGGL(block_select_kernel, dim3((unsigned)((size_t)P.Hq * nb)), dim3(256), 0, s, scores, keep, nb,
                        Pp, mode, topk, topp, keep_diag);
-    return hipGetLastError();
+    return (int)hipGetLastError();
 }
 
 }  // namespace mlct
