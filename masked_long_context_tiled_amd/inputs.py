@@ -138,6 +138,31 @@ def attention_inputs(seed: int, T: int, Hq: int, Hk: int, d: int = 128,
     return out
 
 
+def attention_inputs_device(seed: int, T: int, Hq: int, Hk: int, device, d: int = 128,
+                            chunk: int = 16384) -> dict:
+    """Q [T][Hq][d], K/V [T][Hk][d], dO [T][Hq][d] as bf16 tensors drawn on ``device``.
+
+    For lengths whose inputs are too large to draw on the host (512K: Q and dO hold 2^32
+    values each): i.i.d. N(0,1) float32 from one ``torch.Generator`` on the device seeded
+    with ``seed``, drawn in the order Q, K, V, dO and, within each tensor, in blocks of
+    ``chunk`` positions, each block rounded to bf16 (round to nearest even) as it is drawn.
+    The same arguments give the same bits on the same software stack; a test copies the
+    rows it checks back to the host for the oracle.
+    """
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    out = {}
+    for name, H in (("q", Hq), ("k", Hk), ("v", Hk), ("do", Hq)):
+        t = torch.empty((T, H, d), dtype=torch.bfloat16, device=device)
+        for r0 in range(0, T, chunk):
+            r1 = min(T, r0 + chunk)
+            t[r0:r1] = torch.randn((r1 - r0, H, d), generator=gen, device=device,
+                                   dtype=torch.float32).to(torch.bfloat16)
+        out[name] = t
+    return out
+
+
 def document_cu_seqlens(seed: int, total: int, lo: int = 512, hi: int = 8192) -> Tuple[int, ...]:
     """Packed-sequence document boundaries.
 

@@ -9,7 +9,8 @@ several tiles; group sizes G = 1, 4, 8, 16 exercise every row-to-head mapping.
 import numpy as np
 import pytest
 
-from masked_long_context_tiled_amd.inputs import MaskSpec, attention_inputs, block_sparse_keep, document_cu_seqlens
+from masked_long_context_tiled_amd.inputs import (MaskSpec, attention_inputs, bf16_bits_to_f32, block_sparse_keep,
+                                                  document_cu_seqlens, f32_to_bf16_bits)
 from oracle.attention import attention_backward
 from oracle.tiles import keep_csc, keep_csr, tile_classes, tile_csc, tile_csr
 
@@ -18,17 +19,22 @@ from gpu_helpers import LSE_TOL, TOL, assert_close, note, oracle_inputs, run_gpu
 pytestmark = pytest.mark.gpu
 
 
-def _check(T, Hq, Hk, spec, keep=None, seed=0, backward=True):
-    note(f"parity T={T} Hq={Hq} Hk={Hk} mask={spec.kind} seed={seed}")
-    r = run_gpu(T, Hq, Hk, spec, keep=keep, seed=seed, backward=backward)
+def _check(T, Hq, Hk, spec, keep=None, seed=0, backward=True, scale=0.0, inputs=None, tols=None):
+    """GPU vs oracle on the same inputs; tols maps o / lse / dq / dk / dv to a bound
+    (default 2e-2, LSE 1e-3)."""
+    note(f"parity T={T} Hq={Hq} Hk={Hk} mask={spec.kind} seed={seed} scale={scale or 'default'}")
+    r = run_gpu(T, Hq, Hk, spec, keep=keep, seed=seed, backward=backward, scale=scale, inputs=inputs)
     x = oracle_inputs(r["inputs"])
-    ref = attention_backward(x["q"], x["k"], x["v"], x["do"], spec, keep=keep)
-    errs = {"o": assert_close("O", r["o"], ref["o"], TOL),
-            "lse": assert_close("LSE", r["lse"], ref["lse"], LSE_TOL)}
+    ref = attention_backward(x["q"], x["k"], x["v"], x["do"], spec, keep=keep,
+                             scale=scale if scale > 0 else None)
+    tol = {"o": TOL, "lse": LSE_TOL, "dq": TOL, "dk": TOL, "dv": TOL}
+    tol.update(tols or {})
+    errs = {"o": assert_close("O", r["o"], ref["o"], tol["o"]),
+            "lse": assert_close("LSE", r["lse"], ref["lse"], tol["lse"])}
     if backward:
-        errs["dq"] = assert_close("dQ", r["dq"], ref["dq"], TOL)
-        errs["dk"] = assert_close("dK", r["dk"], ref["dk"], TOL)
-        errs["dv"] = assert_close("dV", r["dv"], ref["dv"], TOL)
+        errs["dq"] = assert_close("dQ", r["dq"], ref["dq"], tol["dq"])
+        errs["dk"] = assert_close("dK", r["dk"], ref["dk"], tol["dk"])
+        errs["dv"] = assert_close("dV", r["dv"], ref["dv"], tol["dv"])
     note("  max errors " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()))
     return r, ref
 
@@ -117,6 +123,92 @@ def test_block_sparse_mha_and_empty_rows():
         assert np.all(r["o"][rows, h] == 0) and np.all(np.isneginf(r["lse"][h, rows]))
         assert np.all(r["dq"][rows, h] == 0)
     assert np.all(r["dk"][9 * b:10 * b] == 0) and np.all(r["dv"][9 * b:10 * b] == 0)
+
+
+def _sparse_keep_with_edge_cases(seed, Hq, Hk, nb):
+    """50 % keep matrix plus the list shapes the block-sparse kernels must handle: a pair of
+    query blocks (0, 1 and 2, 3 pair up at b = 64) with no visible key at all, a block with
+    an empty list beside a non-empty partner, a key block no head of a KV group keeps
+    (dK = dV = 0 there) and a key block kept by one (head, query block) of its group only."""
+    G = Hq // Hk
+    keep = block_sparse_keep(seed, Hq, nb, nb)
+    keep[1, 2:4, :] = 0
+    keep[G - 1, 1, :] = 0
+    keep[0:G, :, 3] = 0
+    last = Hq - G
+    keep[last:Hq, :, nb - 1] = 0
+    keep[last + 1, nb // 2, nb - 1] = 1
+    return keep
+
+
+@pytest.mark.parametrize("b", [64, 128])
+def test_block_sparse_gqa8_edge_lists(b):
+    # G = 8, the workloads' group size: element-wise dK / dV of the key-block-major kernel
+    T, Hq, Hk = 1000, 16, 2
+    nb = -(-T // b)
+    keep = _sparse_keep_with_edge_cases(15, Hq, Hk, nb)
+    r, ref = _check(T, Hq, Hk, MaskSpec("block_sparse", sparse_block=b), keep=keep, seed=15)
+    assert np.all(r["o"][2 * b:4 * b, 1] == 0) and np.all(r["dq"][2 * b:4 * b, 1] == 0)
+    assert np.all(r["dk"][3 * b:4 * b, 0] == 0) and np.all(r["dv"][3 * b:4 * b, 0] == 0)
+
+
+@pytest.mark.parametrize("b,T", [(64, 8192), (128, 4096)])
+def test_block_sparse_long_gqa8(b, T):
+    # 8 query heads on one KV head (G = 8): CSC lists of up to 8 * 64 (query head, query
+    # block) entries per key block, element-wise dK / dV over the whole sequence
+    Hq, Hk = 8, 1
+    nb = T // b
+    keep = _sparse_keep_with_edge_cases(16, Hq, Hk, nb)
+    r, ref = _check(T, Hq, Hk, MaskSpec("block_sparse", sparse_block=b), keep=keep, seed=16)
+    assert np.all(r["dk"][3 * b:4 * b] == 0) and np.all(r["dv"][3 * b:4 * b] == 0)
+
+
+@pytest.mark.parametrize("scale", [0.05, 0.125])
+@pytest.mark.parametrize("kind", ["causal_document", "block_sparse"])
+def test_nondefault_scale(kind, scale):
+    # the forward folds the scale into its exponent, the backward into dS and the unscaling
+    # of dK / dQ: a scale other than 1/sqrt(128) must reach every one of them (a scale lost
+    # or applied twice moves every output by a large fraction of its size). Both scales keep
+    # the scores' spread near the pages' 1/sqrt(128), for which the 2e-2 bound is set.
+    T, Hq, Hk = 1000, 8, 2
+    if kind == "block_sparse":
+        keep = block_sparse_keep(31, Hq, -(-T // 64), -(-T // 64))
+        _check(T, Hq, Hk, MaskSpec("block_sparse", sparse_block=64), keep=keep, seed=31, scale=scale)
+    else:
+        spec = MaskSpec("causal_document", cu_seqlens=document_cu_seqlens(32, T, 64, 400))
+        _check(T, Hq, Hk, spec, seed=32, scale=scale)
+
+
+def _with_outlier_channels(x, chans, factor=1000.0):
+    """Copy of the bf16 inputs with the given channels of each tensor multiplied by factor
+    (then rounded to bf16 again)."""
+    out = {}
+    for n, bits in x.items():
+        f = bf16_bits_to_f32(bits)
+        f[..., chans[n]] *= factor
+        out[n] = f32_to_bf16_bits(f)
+    return out
+
+
+def test_outlier_channels_fp16_scaling():
+    """Q, K, V and dO each carry three channels about 10^3 times larger than the rest. The
+    backward's fp16 operands are scaled by powers of two from the tensors' maxima, so the
+    ordinary channels (10^3 below the maximum) must keep their precision. The 2e-2 bound is
+    for N(0, 1) inputs; here each output's bound is scaled by how much larger that output is
+    than in the same problem without outliers (both from the oracle), which is the same
+    bound for a result whose magnitude the outliers have changed."""
+    T, Hq, Hk = 1000, 8, 2
+    spec = MaskSpec("causal")
+    x = attention_inputs(33, T, Hq, Hk)
+    chans = {"q": [5, 77, 120], "k": [9, 40, 99], "v": [3, 64, 127], "do": [17, 50, 88]}
+    xo = _with_outlier_channels(x, chans)
+    plain = attention_backward(*(oracle_inputs(x)[n] for n in ("q", "k", "v", "do")), spec)
+    outl = attention_backward(*(oracle_inputs(xo)[n] for n in ("q", "k", "v", "do")), spec)
+    ratio = {n: max(1.0, float(np.abs(outl[n]).max() / np.abs(plain[n]).max())) for n in ("o", "dq", "dk", "dv")}
+    ratio["lse"] = max(1.0, float(np.abs(outl["lse"]).max() / np.abs(plain["lse"]).max()))
+    note("outlier ratios " + " ".join(f"{k}={v:.1f}" for k, v in ratio.items()))
+    tols = {n: (LSE_TOL if n == "lse" else TOL) * ratio[n] for n in ratio}
+    _check(T, Hq, Hk, spec, seed=33, inputs=xo, tols=tols)
 
 
 # --- tile index / block index: bit-exact ---------------------------------------------
