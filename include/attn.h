@@ -279,6 +279,26 @@ attn_status attn_block_select(const attn_problem* prob, const attn_block_select_
                               void* stream);
 
 /*
+ * attn_block_select for callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops and harnesses that forbid allocation): the same selection, with
+ * the same kernels and bit-identical results, but no workspace argument. The block means
+ * live in a static device array of ATTN_SELECT_SCRATCH_BYTES (32 MiB), which every GPU the
+ * library runs on holds from the module's load until the process ends; the first call on a
+ * GPU looks up the array's device address (hipGetSymbolAddress; no allocation), later calls
+ * reuse it. Nothing in the array needs clearing between calls (each call writes every mean
+ * it reads). Calls on one GPU share the array and keep the last call's contents: calls that
+ * overlap in time on one GPU (on different streams, or from several host threads) race and
+ * must be serialised by the caller. Arguments and errors as attn_block_select, plus
+ * ATTN_ERR_WORKSPACE when attn_block_select_workspace_size exceeds
+ * ATTN_SELECT_SCRATCH_BYTES (64 query heads at T = 64K with b = 128 need 18.9 MB; with
+ * b = 64, 37.7 MB exceeds it): nothing is launched then.
+ */
+#define ATTN_SELECT_SCRATCH_BYTES (32u << 20)
+attn_status attn_block_select_noalloc(const attn_problem* prob, const attn_block_select_params* sp,
+                                      const void* q, const void* k, float* scores, uint8_t* keep_out,
+                                      void* stream);
+
+/*
  * Variable Block mask (section 三 "注意力掩码模式", 动态掩码: block-sparse with variable
  * block sizes; no further definition on the pages). Row block r covers query positions
  * [row_off[r], row_off[r+1]), column block c key positions [col_off[c], col_off[c+1]), and

@@ -111,6 +111,8 @@ _SIGS = {
     "attn_block_select_workspace_size": (ctypes.c_int, [_PROB, ctypes.POINTER(_SZ)]),
     "attn_block_select": (ctypes.c_int, [_PROB, ctypes.POINTER(attn_block_select_params), _P, _P, _P, _P, _P,
                                          _SZ, _P]),
+    "attn_block_select_noalloc": (ctypes.c_int, [_PROB, ctypes.POINTER(attn_block_select_params), _P, _P, _P, _P,
+                                                 _P]),
     "attn_variable_block_expand": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, _P, ctypes.c_int32, _P,
                                                   ctypes.c_int32, _P, _P]),
 }
@@ -285,6 +287,12 @@ def block_select_workspace_size(prob) -> int:
 def block_select(prob, params, q, k, scores, keep, ws, ws_bytes, stream=0):
     _check(lib().attn_block_select(ctypes.byref(prob), ctypes.byref(params), q, k, scores, keep, ws, ws_bytes,
                                    stream), "attn_block_select")
+
+
+def block_select_noalloc(prob, params, q, k, scores, keep, stream=0):
+    """attn_block_select with the library's static per-GPU workspace (no allocation)."""
+    _check(lib().attn_block_select_noalloc(ctypes.byref(prob), ctypes.byref(params), q, k, scores, keep, stream),
+           "attn_block_select_noalloc")
 
 
 def variable_block_expand(T: int, Hq: int, row_offsets, col_offsets, keep_var: np.ndarray) -> np.ndarray:

@@ -308,6 +308,16 @@ attn_status attn_block_select(const attn_problem* prob, const attn_block_select_
                                           stream));
 }
 
+attn_status attn_block_select_noalloc(const attn_problem* prob, const attn_block_select_params* sp, const void* q,
+                                      const void* k, float* scores, uint8_t* keep_out, void* stream) {
+    Problem P;
+    attn_status st = validate_select(prob, sp, q, k, scores, keep_out, &P);
+    if (st != ATTN_OK) return st;
+    if (select_workspace_bytes(P) > SEL_SCRATCH_BYTES) return ATTN_ERR_WORKSPACE;
+    return hip_status(launch_block_select_scratch(P, sp->mode, sp->topk < P.nb ? sp->topk : P.nb, sp->topp,
+                                                  sp->keep_diagonal ? 1 : 0, q, k, scores, keep_out, stream));
+}
+
 // Block edges 0 = off[0] < off[1] < ... < off[n] = T, the interior ones multiples of 64.
 static bool valid_edges(const int32_t* off, int32_t n, int32_t T) {
     if (!off || n < 1 || off[0] != 0 || off[n] != T) return false;

@@ -84,6 +84,12 @@ int launch_bwd_main(const Problem& P, const void* q, const void* k, const void* 
 int launch_cast_bf16(const float* in, void* out, size_t n, void* stream);
 int launch_block_select(const Problem& P, int mode, int topk, float topp, int keep_diag, const void* q,
                         const void* k, float* scores, uint8_t* keep, void* ws, void* stream);
+// The same launches with the workspace in the library's static per-GPU array (at most
+// SEL_SCRATCH_BYTES; the caller checks the size first). Looks the array up on the device
+// of the stream at its first use there.
+constexpr size_t SEL_SCRATCH_BYTES = size_t(ATTN_SELECT_SCRATCH_BYTES);
+int launch_block_select_scratch(const Problem& P, int mode, int topk, float topp, int keep_diag, const void* q,
+                                const void* k, float* scores, uint8_t* keep, void* stream);
 int launch_lse_merge(const Problem& P, void* o, void* o_lo, float* lse, const void* o_part,
                      const void* o_part_lo, const float* lse_part, void* stream);
 

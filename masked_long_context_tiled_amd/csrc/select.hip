@@ -11,6 +11,8 @@
 //
 // Every score is a sequential fp32 FMA chain over the 128 dimensions, so the scores (and
 // the selection, which only compares them) are deterministic.
+#include <mutex>
+
 #include "common.h"
 
 namespace mlct {
@@ -220,6 +222,47 @@ int launch_block_select(const Problem& P, int mode, int topk, float topp, int ke
     hipLaunchKernelGGL(block_select_kernel, dim3((unsigned)((size_t)P.Hq * nb)), dim3(256), 0, s, scores, keep, nb,
                        Pp, mode, topk, topp, keep_diag);
     return (int)hipGetLastError();
+}
+
+// Workspace of attn_block_select_noalloc: one static array on every GPU the library runs on.
+// In host code the array's name stands for a host-side shadow, so its device address is
+// looked up (hipGetSymbolAddress) once per device, with that device current, and only that
+// address is ever passed to a kernel.
+static __device__ __align__(256) unsigned char scratch[SEL_SCRATCH_BYTES];
+
+constexpr int SCRATCH_MAX_DEVICES = 64;
+static std::mutex scratch_mu;
+static void* scratch_dev[SCRATCH_MAX_DEVICES];
+
+static hipError_t scratch_address(hipStream_t s, void** out) {
+    int cur = 0, dev = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    dev = cur;
+    if (s != nullptr && (e = hipStreamGetDevice(s, &dev)) != hipSuccess) return e;
+    if (dev < 0 || dev >= SCRATCH_MAX_DEVICES) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_dev[dev]) {
+        if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur) {
+            const hipError_t e2 = hipSetDevice(cur);
+            if (e == hipSuccess) e = e2;
+        }
+        if (e != hipSuccess) return e;
+        scratch_dev[dev] = p;
+    }
+    *out = scratch_dev[dev];
+    return hipSuccess;
+}
+
+int launch_block_select_scratch(const Problem& P, int mode, int topk, float topp, int keep_diag, const void* q,
+                                const void* k, float* scores, uint8_t* keep, void* stream) {
+    void* ws = nullptr;
+    const hipError_t e = scratch_address(static_cast<hipStream_t>(stream), &ws);
+    if (e != hipSuccess) return (int)e;
+    return launch_block_select(P, mode, topk, topp, keep_diag, q, k, scores, keep, ws, stream);
 }
 
 }  // namespace mlct

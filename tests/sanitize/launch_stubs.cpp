@@ -26,6 +26,8 @@ int launch_bwd_main(const Problem&, const void*, const void*, const void*, const
 int launch_cast_bf16(const float*, void*, size_t, void*) { no_gpu(__func__); }
 int launch_block_select(const Problem&, int, int, float, int, const void*, const void*, float*, uint8_t*, void*,
                         void*) { no_gpu(__func__); }
+int launch_block_select_scratch(const Problem&, int, int, float, int, const void*, const void*, float*, uint8_t*,
+                                void*) { no_gpu(__func__); }
 int launch_lse_merge(const Problem&, void*, void*, float*, const void*, const void*, const float*, void*) {
     no_gpu(__func__);
 }

@@ -185,3 +185,17 @@ def test_desc_equals_predicate_workloads(name):
     got = _desc_dense(desc, rows)
     want = mask_block(wl.mask, wl.T, rows, np.arange(wl.T))
     assert np.array_equal(got, want)
+
+
+def test_block_select_noalloc_rejects_beyond_static_array():
+    # 64 query heads at T = 64K with b = 64 need 37.7 MB of block means, more than the 32 MiB
+    # static array: rejected before any device call (no GPU needed)
+    prob = attn.problem(65536, 64, 8, "block_sparse", 64)
+    assert attn.block_select_workspace_size(prob) > (32 << 20)
+    params = attn.block_select_params("topk", topk=4)
+    fake = ctypes.c_void_p(256)
+    L = attn.lib()
+    assert L.attn_block_select_noalloc(ctypes.byref(prob), ctypes.byref(params), fake, fake, fake, fake,
+                                       None) == attn.ATTN_ERR_WORKSPACE
+    assert L.attn_block_select_noalloc(ctypes.byref(prob), None, fake, fake, fake, fake,
+                                       None) == attn.ATTN_ERR_INVALID_ARG
