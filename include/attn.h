@@ -392,7 +392,10 @@ attn_status attn_bwd_dq(const attn_problem* prob, const void* q, const void* k, 
                         const int32_t* desc_dev, const void* index_dev, size_t index_bytes,
                         const void* ws, size_t ws_bytes, void* stream);
 
-/* Optional cast of fp32 gradients to bf16 (round to nearest even): out[i] = bf16(in[i]). */
+/* Optional cast of fp32 gradients to bf16: out[i] = bf16(in[i]), rounded to nearest with ties
+ * to even (the largest finite values round to infinity; infinities keep their sign; a NaN
+ * gives a NaN; subnormals are rounded, not flushed). in: device fp32 [n]; out: device bf16
+ * [n]. n = 0 is a no-op; null pointers with n > 0 give ATTN_ERR_INVALID_ARG. */
 attn_status attn_cast_bf16(const float* in, void* out, size_t n, void* stream);
 
 #ifdef __cplusplus

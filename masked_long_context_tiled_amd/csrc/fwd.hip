@@ -4,8 +4,9 @@
 // 64-key tiles. Dense masks (fwd_dense_kernel, NW = 8): the rows are the G query heads
 // of one KV head times 256/G consecutive positions (one query tile of the tile index),
 // so every K/V tile staged in LDS is reused by the whole GQA group. Block-sparse
-// (fwd_sparse_kernel, NW = b/32): the rows are one (query head, query block) row of the
-// keep matrix.
+// (fwd_sparse_kernel, four waves): at b = 128 the rows are one (query head, query block)
+// row of the keep matrix; at b = 64 they are two such rows of one head (query blocks 2p
+// and 2p + 1), which walk the union of their key lists.
 //
 // Each wave owns 32 rows and computes the transposed scores S^T = K Q^T with
 // v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = Q held in registers), so a lane holds
@@ -48,8 +49,9 @@ struct FwdArgs {
 constexpr int K_LD = HEAD_DIM + 8;    // bf16 per K row in LDS
 constexpr int V_LD = HEAD_DIM + 16;   // bf16 per V row in LDS
 
-// Block-sparse work items: one (query head, query block) row of the keep matrix, b/32
-// waves, each list entry a b-key block walked as b/64 tiles. K and V are staged row-major
+// Block-sparse work items, four waves: at b = 128 one (query head, query block) row of the
+// keep matrix, each list entry a 128-key block walked as two 64-key tiles; at b = 64 (PAIR,
+// below) two rows, each list entry one 64-key tile. K and V are staged row-major
 // (V^T read with transposed LDS reads, as in the dense kernel), single-buffered with two
 // barriers per tile (the small LDS footprint keeps four work items per CU).
 //
@@ -124,8 +126,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_sparse_kernel(FwdArgs a) {
     u32x4 kreg[CPT], vreg[CPT];
     int nkey0 = 0;
     // the fixed part of each chunk's offset: chunk c = tid + i * NT is row c / 16 of the
-    // tile, dims 8 (c % 16) .. + 7 (b = 128 only: at b = 64 the eight offsets per thread
-    // would cost the kernel its second wave per SIMD)
+    // tile, dims 8 (c % 16) .. + 7 (every instance launched has four waves, so both block
+    // sizes use it; a two-wave instance would need eight offsets per thread, which would
+    // cost it its second wave per SIMD)
     constexpr bool FIXED_OFS = NW == 4;
     unsigned lofs[CPT];
 #pragma unroll
