@@ -243,10 +243,13 @@ __device__ __forceinline__ RowMap row_map(const BwdArgs& a, int g, int e) {
 // The roles run one step apart, so a step (32 query rows) needs a single barrier:
 //   step s, A: dV^T += dO_s^T P_s (P_s kept in registers from step s - 1),
 //              S and P of step s + 1 (P -> LDS slot (s+1)%2 and registers),
-//              stage Q, LSE of step s + 2 into Q slot (s+2)%3, load step s + 3;
+//              stage Q, LSE of step s + 2 into Q slot (s+2)%3, load step s + 2 + PD;
 //   step s, B: dS_s = P_s * (dP_s - D_s) with P_s from LDS slot s%2 and dP_s kept in
 //              registers from step s - 1, dK^T += Q_s^T dS_s, then dP_{s+1} = dO_{s+1} V^T,
-//              stage dO, D of step s + 2 into slot (s+2)%3, load step s + 3.
+//              stage dO, D of step s + 2 into slot (s+2)%3, load step s + 2 + PD.
+// The row loads run PD steps ahead of their stores (PD = 2 for the dense masks, whose
+// 256-row tiles stream from HBM, with two register stages; 1 for block-sparse), so a
+// load has PD whole steps to arrive before the store waits for it.
 // Each wave thus alternates a vector phase with a run of 16 MFMAs, in opposite order to its
 // partner on the SIMD: B forms dS while A issues its dV and S MFMAs, and A forms P while B
 // issues its dK and dP MFMAs.
@@ -322,22 +325,28 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
     int4 kd = {0, 0, 0, 0};
     if (!SPARSE && is_a && key_ok) kd = a.desc[my_key];
 
-    EntryStream es;
+    EntryStream es;           // list entries of the staged row loads (2 + PD steps ahead)
     es.init(a.ent, lb, le - lb, lane);
-    int e_q0 = 0, e_q1 = 0;   // A: list entries of the two most recently loaded steps
+    EntryStream esc;          // A: list entries of the steps whose P it forms
+    esc.init(a.ent, lb, le - lb, lane);
 
     // Staging of this role's tensor (A: Q and LSE, B: dO and D). Rows past the end are
     // read from a valid row and get LSE = +inf (P = 0) and D = 0 when stored.
     const _Float16* src = is_a ? a.qh : a.doh;
     const float* ssrc = is_a ? a.lse : a.dbuf;
     const int span = SPARSE ? a.sblock : a.BMq;   // positions per list entry
-    u32x4 pre[CPT];
-    float praw = 0.f;
-    bool pvalid = false;
-    auto load_rows = [&](int st) {
+    // rows in flight: PD register stages, loaded PD steps before they are stored (two for the
+    // dense masks, whose long lists of 256-row tiles stream from HBM; one for block-sparse,
+    // where the b = 64 instance is at the two-waves-per-SIMD register limit and b = 128 gains
+    // nothing)
+    constexpr int PD = (NWK == 4 && !SPARSE) ? 2 : 1;
+    using Second = BoolTag<PD == 2>;   // register stage of odd steps
+    u32x4 pre[2][CPT];
+    float praw[2] = {0.f, 0.f};
+    bool pvalid[2] = {false, false};
+    auto load_rows = [&](int st, auto bt) {
+        constexpr int BUF = decltype(bt)::value;
         const int e = es.get(st >> lgRB, lane), rb = st & (RB - 1);
-        e_q0 = e_q1;
-        e_q1 = e;
         const RowMap m = row_map<SPARSE>(a, g, e);
         if (m.pbase + span <= T) {
             // one base per step plus small per-lane offsets
@@ -346,36 +355,38 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
             for (int i = 0; i < CPT; ++i) {
                 const int c = rt + i * NR, R = rb * 32 + (c >> 4);
                 const unsigned off = (unsigned)((((R & m.mask) * a.Hq + (R >> m.lg)) * HEAD_DIM) + (c & 15) * 8);
-                pre[i] = *reinterpret_cast<const u32x4*>(base + off);
+                pre[BUF][i] = *reinterpret_cast<const u32x4*>(base + off);
             }
         } else {
 #pragma unroll
             for (int i = 0; i < CPT; ++i) {
                 const int c = rt + i * NR, R = rb * 32 + (c >> 4);
                 const int p = min(m.pos(R), T - 1);
-                pre[i] = *reinterpret_cast<const u32x4*>(src + ((size_t)p * a.Hq + m.head(R)) * HEAD_DIM + (c & 15) * 8);
+                pre[BUF][i] = *reinterpret_cast<const u32x4*>(src + ((size_t)p * a.Hq + m.head(R)) * HEAD_DIM + (c & 15) * 8);
             }
         }
         if (rt < 32) {
             const int R = rb * 32 + rt, p = m.pos(R);
-            pvalid = p < T;
-            praw = ssrc[(size_t)m.head(R) * T + min(p, T - 1)];
+            pvalid[BUF] = p < T;
+            praw[BUF] = ssrc[(size_t)m.head(R) * T + min(p, T - 1)];
         }
     };
-    auto store_rows = [&](int slot) {
+    auto store_rows = [&](int slot, auto bt) {
+        constexpr int BUF = decltype(bt)::value;
         _Float16* dst = is_a ? Qh[slot] : dOh[slot];
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const int c = rt + i * NR;
-            *reinterpret_cast<u32x4*>(&dst[roff(c >> 4, (c & 15) * 8)]) = pre[i];
+            *reinterpret_cast<u32x4*>(&dst[roff(c >> 4, (c & 15) * 8)]) = pre[BUF][i];
         }
         if (rt < 32) {
             if (is_a)
-                lse_s[slot][rt] = (!pvalid || praw == -INFINITY) ? INFINITY : praw * LOG2E;
+                lse_s[slot][rt] = (!pvalid[BUF] || praw[BUF] == -INFINITY) ? INFINITY : praw[BUF] * LOG2E;
             else
-                dd_s[slot][rt] = pvalid ? praw * sO : 0.f;
+                dd_s[slot][rt] = pvalid[BUF] ? praw[BUF] * sO : 0.f;
         }
     };
+    constexpr BoolTag<false> B0{};
 
     // A: S = Q K^T and P for step st (entry e) from Q slot qs; P -> LDS slot st % 2 and pb.
     // P slots (hf, e) of 16-row step kk are rows 16*kk + 8*(e/4) + 4*hf + e%4.
@@ -461,11 +472,11 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
     // prologue: A stages Q_0 and Q_1, B stages dO_0 and dO_1; then A forms P_0 and B dP_0,
     // and both load the rows of step 2
     if (nsteps > 0) {
-        load_rows(0);
-        store_rows(0);
+        load_rows(0, B0);
+        store_rows(0, B0);
         if (nsteps > 1) {
-            load_rows(1);
-            store_rows(1);
+            load_rows(1, Second{});
+            store_rows(1, Second{});
         }
     }
     lds_barrier();
@@ -474,18 +485,18 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
     if (nsteps > 0) {
         // settle the one-time loads here, so no step waits for them behind its prefetches
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        if (is_a) s_and_p(0, nsteps > 1 ? e_q0 : e_q1, 0, pb_cur);   // loads so far: steps 0 and 1
+        if (is_a) s_and_p(0, esc.get(0, lane), 0, pb_cur);
         else dpacc = dp_of(0);
-        if (nsteps > 2) load_rows(2);
+        // register stage (s % PD) holds the rows of step s + 2 at the top of step s
+        if (nsteps > 2) load_rows(2, B0);
+        if (PD == 2 && nsteps > 3) load_rows(3, Second{});
     }
     lds_barrier();
 
     if (is_a) {
-        // At the top of step s the last two loads were of steps s + 1 and s + 2 (e_q0, e_q1),
-        // or of steps s and s + 1 when s + 2 is past the end.
         int qs1 = 1;   // Q slot of step s + 1
         int os = 0;    // dO slot of step s
-        for (int step = 0; step < nsteps; ++step) {
+        auto a_step = [&](int step, auto bt) {
             // dV^T += (dO * sO)^T P of this step first (P from the previous step), then S and
             // P of the next step: the exponentials then run while the B wave on the same SIMD
             // issues its dK and dP MFMAs, and B's dS work while this wave issues MFMAs
@@ -493,18 +504,22 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
             mfma_pipelined<8>(
                 [&](int i) { return rtr(doh, 16 * (i & 1), (i >> 1) * 32, lane); },
                 [&](int i, u32x4 op) { acc[i >> 1] = mfma32h(as_f16x8(op), pb_cur[i & 1], acc[i >> 1]); });
-            if (step + 1 < nsteps) s_and_p(step + 1, step + 2 < nsteps ? e_q0 : e_q1, qs1, pb_cur);
+            if (step + 1 < nsteps) s_and_p(step + 1, esc.get((step + 1) >> lgRB, lane), qs1, pb_cur);
 
             const int qs2 = qs1 == 2 ? 0 : qs1 + 1;   // Q slot of step s + 2
-            if (step + 2 < nsteps) store_rows(qs2);
-            if (step + 3 < nsteps) load_rows(step + 3);
+            if (step + 2 < nsteps) store_rows(qs2, bt);
+            if (step + 2 + PD < nsteps) load_rows(step + 2 + PD, bt);
             qs1 = qs2;
             os = os == 2 ? 0 : os + 1;
             lds_barrier();
+        };
+        for (int step = 0; step < nsteps; step += 2) {
+            a_step(step, B0);
+            if (step + 1 < nsteps) a_step(step + 1, Second{});
         }
     } else {
         int qs0 = 0;   // Q and dO slot of step s
-        for (int step = 0; step < nsteps; ++step) {
+        auto b_step = [&](int step, auto bt) {
             const int cb = step & 1;
             // dS * sO = P * (dP * sO - D * sO); dK^T += (Q * sQ)^T (dS * sO)
             f16x8 sb[2];
@@ -538,10 +553,14 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
             const int qs1 = qs0 == 2 ? 0 : qs0 + 1, qs2 = qs1 == 2 ? 0 : qs1 + 1;
             // dP of the next step (its dO rows were staged a step earlier)
             if (step + 1 < nsteps) dpacc = dp_of(qs1);
-            if (step + 2 < nsteps) store_rows(qs2);
-            if (step + 3 < nsteps) load_rows(step + 3);
+            if (step + 2 < nsteps) store_rows(qs2, bt);
+            if (step + 2 + PD < nsteps) load_rows(step + 2 + PD, bt);
             qs0 = qs1;
             lds_barrier();
+        };
+        for (int step = 0; step < nsteps; step += 2) {
+            b_step(step, B0);
+            if (step + 1 < nsteps) b_step(step + 1, Second{});
         }
     }
 
