@@ -41,7 +41,7 @@ from masked_long_context_tiled_amd.inputs import MaskSpec, attention_inputs, kee
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0
 METRIC = "effective attn TFLOPs fwd/bwd, 8K GQA 64:8 hd128 bf16 per mask; % MFMA peak"
-KERNEL_SOURCES = ["fwd.hip", "bwd.hip", "index.hip", "common.h"]
+KERNEL_SOURCES = ["fwd.hip", "bwd.hip", "index.hip", "common.h", "host.h"]
 
 
 def log(msg):
@@ -393,6 +393,12 @@ def main():
                      "achieved": round(dkdv_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(dkdv_tf / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_for(wl.name, "bwd_kernel"),
+                     # not measured in this run: HBM bytes per launch from the committed
+                     # rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of this workload, valid only
+                     # while the kernel sources hash the same (null otherwise)
+                     "traffic_source": (f"profiles/traffic_bwd_kernel_{wl.name}.json (rocprofv3 --pmc, "
+                                        f"kernel hash {kernel_hash()})"
+                                        if traffic_for(wl.name, "bwd_kernel") is not None else None),
                      "avg_launch_ms": round(mean["bwd_dkdv"], 4),
                      "flops_per_launch": dkdv_flops},
         "kernel_hash": kernel_hash(),
