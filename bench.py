@@ -2,10 +2,12 @@
 """Throughput of the masked attention hot path on one MI355X (gfx950).
 
 One step = one pass of the whole path over one batch of synthetic inputs that are
-already resident in HBM:
-  column-interval descriptor (host) -> device copy -> tile index (classifier + lists)
+already resident in HBM (the document boundaries of the DOCUMENT masks included):
+  column-interval descriptor (built on the device) -> tile index (classifier + lists)
   -> attn_fwd -> attn_bwd_preprocess (D = rowsum(dO*O), operand bounds)
   -> attn_bwd_dkdv (dK, dV) -> attn_bwd_dq (dQ).
+The step's launches are captured once into a HIP graph and the timed steps replay it
+(--no-graph: the same launches issued one by one in every step).
 Block-sparse workloads replace the first two steps by the block index of a keep matrix
 uploaded once; dynamic block-sparse workloads select that keep matrix from Q and K
 (attn_block_select, TopK / TopP) in every step; the variable-block workload expands its
@@ -200,6 +202,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-heads", type=int, default=2, help="query heads in the oracle timing sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="launch each step's kernels one by one instead of replaying a captured HIP graph")
     ap.add_argument("--out", default=None, help="also append the JSON line to this file")
     ap.add_argument("--sweep", action="store_true",
                     help="sequence-length sweep (1K .. --sweep-max, powers of two) of one mask at GQA 64:8: "
@@ -278,41 +282,51 @@ def main():
     dv = torch.empty((T, Hk, d), dtype=torch.float32, device=dev)
     ws_bytes = attn.bwd_workspace_size(prob)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    cu_dev = None
+    if not sparse and spec.cu_seqlens:
+        # the document boundaries are an input of the problem, resident like Q, K, V
+        cu_dev = torch.tensor(spec.cu_seqlens, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev)
-    sp = stream.cuda_stream
 
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(7)]
     times = {"select": [], "index": [], "fwd": [], "bwd_pre": [], "bwd_dkdv": [], "bwd_dq": []}
 
     def step(record: bool):
+        cur = torch.cuda.current_stream(dev)   # the capture stream inside a graph
+        sp = cur.cuda_stream
+
+        def mark(i):
+            if record:
+                ev[i].record(cur)
+
         if sparse:
-            ev[6].record(stream)
+            mark(6)
             if dynamic:
                 attn.block_select(prob, sel_params, q.data_ptr(), k.data_ptr(), scores.data_ptr(),
                                   keep_dev.data_ptr(), sel_ws.data_ptr(), sel_bytes, sp)
-            ev[0].record(stream)
+            mark(0)
             attn.block_index_build(prob, keep_dev.data_ptr(), index.data_ptr(), idx_bytes, sp)
         else:
-            dh = attn.mask_desc_build(spec, T)                     # a1 (host)
-            desc_dev.copy_(torch.from_numpy(dh))                   # synchronous, 16 B per key
-            ev[6].record(stream)
-            ev[0].record(stream)
+            mark(6)
+            mark(0)
+            attn.mask_desc_build_device(spec, T, 0 if cu_dev is None else cu_dev.data_ptr(),
+                                        desc_dev.data_ptr(), sp)                                # a1 (device)
             attn.tile_index_build(prob, desc_dev.data_ptr(), index.data_ptr(), idx_bytes, sp)   # a2
-        ev[1].record(stream)
+        mark(1)
         attn.fwd(prob, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), o_lo.data_ptr(), lse.data_ptr(),
                  0 if sparse else desc_dev.data_ptr(), index.data_ptr(), idx_bytes, 0, 0, sp)       # a3
-        ev[2].record(stream)
+        mark(2)
         attn.bwd_preprocess(prob, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), o_lo.data_ptr(),
                             do.data_ptr(), ws.data_ptr(), ws_bytes, sp)                                     # a4
-        ev[3].record(stream)
+        mark(3)
         attn.bwd_dkdv(prob, q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(), do.data_ptr(),
                       dk.data_ptr(), dv.data_ptr(), 0 if sparse else desc_dev.data_ptr(),
                       index.data_ptr(), idx_bytes, ws.data_ptr(), ws_bytes, sp)                     # a5 (dK, dV)
-        ev[4].record(stream)
+        mark(4)
         attn.bwd_dq(prob, q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(), do.data_ptr(),
                     dq.data_ptr(), 0 if sparse else desc_dev.data_ptr(),
                     index.data_ptr(), idx_bytes, ws.data_ptr(), ws_bytes, sp)                       # a5 (dQ)
-        ev[5].record(stream)
+        mark(5)
         if record:
             ev[5].synchronize()
             times["select"].append(ev[6].elapsed_time(ev[0]))
@@ -335,12 +349,26 @@ def main():
     fwd_flops = 4.0 * d * (U_all if U_all is not None else Hq * U)
     bwd_flops = 2.5 * fwd_flops
 
+    # one step's launches captured into a HIP graph, replayed by the timed steps (the same
+    # kernels on the same buffers; --no-graph launches them one by one instead)
+    graph = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step(False)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+
     # timed region: exactly K steps, synchronised on both sides
-    log(f"timing {args.steps} steps")
+    log(f"timing {args.steps} steps ({'graph replays' if graph is not None else 'eager launches'})")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step(False)
+        if graph is not None:
+            graph.replay()
+        else:
+            step(False)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = 1e3 * wall / args.steps
@@ -378,6 +406,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "mask": spec.kind, "T": T, "Hq": Hq, "Hk": Hk, "head_dim": d,
                    "global_batch": 1, "seq_len": T, "parallelism": "none", "seed": args.seed,
+                   "launch": "hip graph" if graph is not None else "eager",
                    **({"select": list(wl.select)} if dynamic else {}),
                    **({"sparse_block": spec.sparse_block} if sparse else {})},
         "visible_pairs_per_head": U,

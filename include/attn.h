@@ -141,6 +141,22 @@ const char* attn_status_string(attn_status s);
 attn_status attn_mask_desc_build(const attn_mask_params* p, int32_t T, int32_t* desc_out);
 
 /*
+ * The same descriptor built on the device (asynchronous on stream): one thread per key
+ * column runs the host builder's per-column rule, so a step that rebuilds its mask needs no
+ * host work and no host-to-device copy, and can be captured in a HIP graph.
+ *   p              : mask parameters, validated on the host as by attn_mask_desc_build
+ *                    (p->cu_seqlens, if the kind uses documents, is read on the host for
+ *                    the validation only)
+ *   cu_seqlens_dev : device int32 [n_docs + 1], the same values as p->cu_seqlens; required
+ *                    by the four DOCUMENT kinds, ignored by the others (may be NULL)
+ *   desc_dev       : device int32 [T][4], written entirely by the launch
+ * Errors: as attn_mask_desc_build, plus ATTN_ERR_INVALID_ARG for a null desc_dev or a
+ * DOCUMENT kind without cu_seqlens_dev (nothing is launched then).
+ */
+attn_status attn_mask_desc_build_device(const attn_mask_params* p, int32_t T, const int32_t* cu_seqlens_dev,
+                                        int32_t* desc_dev, void* stream);
+
+/*
  * Context-parallel building block (the pages' ring / USP / LoongTrain methods exchange
  * K/V chunks of one long sequence between devices and combine per-chunk results; see
  * "LongCA-bench: 长上下文注意力基准测试", section 三 "分布式注意力机制" and section 四

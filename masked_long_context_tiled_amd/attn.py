@@ -105,6 +105,7 @@ _SIGS = {
     "attn_bwd_dkdv": (ctypes.c_int, [_PROB, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _SZ, _P]),
     "attn_bwd_dq": (ctypes.c_int, [_PROB, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _SZ, _P]),
     "attn_cast_bf16": (ctypes.c_int, [_P, _P, _SZ, _P]),
+    "attn_mask_desc_build_device": (ctypes.c_int, [ctypes.POINTER(attn_mask_params), ctypes.c_int32, _P, _P, _P]),
     "attn_mask_desc_build_chunk": (ctypes.c_int, [ctypes.POINTER(attn_mask_params), ctypes.c_int32, ctypes.c_int32,
                                                   ctypes.c_int32, ctypes.c_int32, _P]),
     "attn_lse_merge": (ctypes.c_int, [_PROB, _P, _P, _P, _P, _P, _P, _P]),
@@ -256,6 +257,14 @@ def bwd_dq(prob, q, k, v, lse, dout, dq, desc, index, index_bytes, ws, ws_bytes,
 
 def cast_bf16(src: int, dst: int, n: int, stream: int = 0):
     _check(lib().attn_cast_bf16(src, dst, n, stream), "attn_cast_bf16")
+
+
+def mask_desc_build_device(spec: MaskSpec, T: int, cu_seqlens_dev: int, desc_dev: int, stream: int = 0):
+    """attn_mask_desc_build_device: the descriptor of spec written to the device buffer
+    desc_dev (int32 [T][4]); cu_seqlens_dev: device copy of spec.cu_seqlens (0 if unused)."""
+    p, keep = mask_params(spec)
+    _check(lib().attn_mask_desc_build_device(ctypes.byref(p), int(T), cu_seqlens_dev or None, desc_dev, stream),
+           "attn_mask_desc_build_device")
 
 
 def mask_desc_build_chunk(spec: MaskSpec, T: int, q_offset: int, k_offset: int, n: int) -> np.ndarray:

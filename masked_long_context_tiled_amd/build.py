@@ -11,7 +11,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libattn.so")
-SOURCES = ["host.cpp", "index.hip", "fwd.hip", "bwd.hip", "merge.hip", "select.hip"]
+SOURCES = ["host.cpp", "desc.hip", "index.hip", "fwd.hip", "bwd.hip", "merge.hip", "select.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -5,6 +5,7 @@
 #include <math.h>
 #include <string.h>
 
+#include "desc.h"
 #include "host.h"
 
 namespace mlct {
@@ -82,106 +83,10 @@ IndexLayout index_layout(const Problem& P) {
     return L;
 }
 
-// ---------------------------------------------------------------------------------
-// Column-interval descriptor: for key column j the visible query rows are
-// [a0, b0) U [a1, b1). Each case below restates the kind's rule from attn.h in
-// column form, for one column of a sequence of length T.
-// ---------------------------------------------------------------------------------
-static void column_intervals(const attn_mask_params* mp, int32_t T, int j, long iv[4]) {
-    const int k = mp->kind;
-    auto set = [&](long a0, long b0, long a1, long b1) {
-        iv[0] = a0;
-        iv[1] = b0;
-        iv[2] = a1;
-        iv[3] = b1;
-    };
-    auto lmin = [](long a, long b) { return a < b ? a : b; };
-    auto lmax = [](long a, long b) { return a > b ? a : b; };
-    // document of j: cu[d] <= j < cu[d + 1]
-    auto doc_of = [&](int x) {
-        int lo = 0, hi = mp->n_docs - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) / 2;
-            if (mp->cu_seqlens[mid] <= x) lo = mid; else hi = mid - 1;
-        }
-        return lo;
-    };
-    switch (k) {
-    case ATTN_MASK_FULL: set(0, T, 0, 0); return;
-    case ATTN_MASK_CAUSAL: set(j, T, 0, 0); return;
-    case ATTN_MASK_FULL_DOCUMENT:
-    case ATTN_MASK_CAUSAL_DOCUMENT: {
-        const int d = doc_of(j);
-        const long s0 = mp->cu_seqlens[d], e0 = mp->cu_seqlens[d + 1];
-        set(k == ATTN_MASK_FULL_DOCUMENT ? s0 : j, e0, 0, 0);
-        return;
-    }
-    case ATTN_MASK_FULL_SLIDING_WINDOW: {
-        const long w = mp->window;
-        set(lmax(0, j - w + 1), lmin(T, j + w), 0, 0);
-        return;
-    }
-    case ATTN_MASK_CAUSAL_SLIDING_WINDOW: set(j, lmin(T, (long)j + mp->window), 0, 0); return;
-    case ATTN_MASK_SHARED_QUESTION: {
-        const long Qn = mp->question_len, A = mp->answer_len;
-        if (j < Qn) set(j, T, 0, 0);                                   // question key: every later row
-        else set(j, lmin(T, Qn + ((j - Qn) / A + 1) * A), 0, 0);       // rest of its answer
-        return;
-    }
-    case ATTN_MASK_PREFIX_LM_CAUSAL: set(j < mp->prefix_len ? 0 : j, T, 0, 0); return;
-    case ATTN_MASK_CAUSAL_BLOCKWISE: {
-        const long b = mp->block_len, F = (long)T - mp->final_block_len;
-        if (j >= F) { set(j, T, 0, 0); return; }
-        const long bend = lmin(T, ((long)j / b + 1) * b);              // rows of j's own block
-        if (bend >= F) set(j, T, 0, 0);                                // touches the final block
-        else set(j, bend, F, T);
-        return;
-    }
-    case ATTN_MASK_GLOBAL_SLIDING: {
-        const long Gl = mp->global_len, w = mp->window;
-        if (j < Gl) { set(0, T, 0, 0); return; }                       // global key: every row
-        const long lo = lmax(0, j - w + 1), hi = lmin(T, j + w);
-        if (lo <= Gl) set(0, lmax(hi, Gl), 0, 0);                      // window meets the global rows
-        else set(0, Gl, lo, hi);
-        return;
-    }
-    case ATTN_MASK_PREFIX_LM_DOCUMENT: {
-        const int d = doc_of(j);
-        const long s0 = mp->cu_seqlens[d], e0 = mp->cu_seqlens[d + 1];
-        set(j - s0 < mp->prefix_len ? s0 : j, e0, 0, 0);               // prefix key: its whole document
-        return;
-    }
-    case ATTN_MASK_BLOCK_CAUSAL_DOCUMENT: {
-        const int d = doc_of(j);
-        const long s0 = mp->cu_seqlens[d], e0 = mp->cu_seqlens[d + 1], b = mp->block_len;
-        set(s0 + (j - s0) / b * b, e0, 0, 0);                          // rows from the start of j's block on
-        return;
-    }
-    default: set(0, 0, 0, 0); return;                                   // not reached: validated first
-    }
-}
-
-// Descriptor of the n x n chunk pair (query rows q_offset.., key columns k_offset..) of
-// a sequence of length T, in chunk coordinates: each global interval is clipped to the
-// query chunk and shifted; empty intervals become [0, 0) and a lone interval comes first.
+// Descriptor of the n x n chunk pair at (q_offset, k_offset), every column (host).
 static void build_desc(const attn_mask_params* mp, int32_t T, int32_t q_offset, int32_t k_offset, int32_t n,
                        int32_t* out) {
-    for (int jl = 0; jl < n; ++jl) {
-        long iv[4];
-        column_intervals(mp, T, k_offset + jl, iv);
-        long a0 = iv[0] - q_offset, b0 = iv[1] - q_offset, a1 = iv[2] - q_offset, b1 = iv[3] - q_offset;
-        a0 = a0 < 0 ? 0 : a0;
-        a1 = a1 < 0 ? 0 : a1;
-        b0 = b0 > n ? n : b0;
-        b1 = b1 > n ? n : b1;
-        if (a0 >= b0) { a0 = b0 = 0; }
-        if (a1 >= b1) { a1 = b1 = 0; }
-        if (a0 == b0 && a1 != b1) { a0 = a1; b0 = b1; a1 = b1 = 0; }
-        out[4 * jl + 0] = (int32_t)a0;
-        out[4 * jl + 1] = (int32_t)b0;
-        out[4 * jl + 2] = (int32_t)a1;
-        out[4 * jl + 3] = (int32_t)b1;
-    }
+    for (int jl = 0; jl < n; ++jl) desc_column(mp, T, q_offset, k_offset, n, jl, out + 4 * jl);
 }
 
 static attn_status validate_mask(const attn_mask_params* mp, int32_t T) {
@@ -248,6 +153,19 @@ attn_status attn_mask_desc_build(const attn_mask_params* p, int32_t T, int32_t* 
     if (st != ATTN_OK) return st;
     build_desc(p, T, 0, 0, T, desc_out);
     return ATTN_OK;
+}
+
+attn_status attn_mask_desc_build_device(const attn_mask_params* p, int32_t T, const int32_t* cu_seqlens_dev,
+                                        int32_t* desc_dev, void* stream) {
+    if (!desc_dev) return ATTN_ERR_INVALID_ARG;
+    attn_status st = validate_mask(p, T);
+    if (st != ATTN_OK) return st;
+    attn_mask_params d = *p;
+    const bool docs = p->kind == ATTN_MASK_FULL_DOCUMENT || p->kind == ATTN_MASK_CAUSAL_DOCUMENT ||
+                      p->kind == ATTN_MASK_PREFIX_LM_DOCUMENT || p->kind == ATTN_MASK_BLOCK_CAUSAL_DOCUMENT;
+    if (docs && !cu_seqlens_dev) return ATTN_ERR_INVALID_ARG;
+    d.cu_seqlens = docs ? cu_seqlens_dev : nullptr;
+    return hip_status(launch_desc(d, T, desc_dev, stream));
 }
 
 attn_status attn_mask_desc_build_chunk(const attn_mask_params* p, int32_t T, int32_t q_offset, int32_t k_offset,

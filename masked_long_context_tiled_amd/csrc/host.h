@@ -71,6 +71,8 @@ constexpr size_t select_workspace_bytes(const Problem& P) {
 // Kernel launchers, defined next to their kernels. Each returns the HIP runtime's error
 // code after queueing its launches (0 = success); stream is a hipStream_t; desc points to
 // the int32 [T][4] column-interval descriptor on the device.
+// The column-interval descriptor of mp (whose cu_seqlens, if used, points to device memory).
+int launch_desc(const attn_mask_params& mp, int32_t T, int32_t* desc, void* stream);
 int launch_index_dense(const Problem& P, const int32_t* desc, void* index, void* stream);
 int launch_index_sparse(const Problem& P, const uint8_t* keep, void* index, void* stream);
 int launch_fwd(const Problem& P, const void* q, const void* k, const void* v, void* o, void* o_lo, float* lse,

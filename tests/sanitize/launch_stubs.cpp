@@ -15,6 +15,7 @@ namespace mlct {
     abort();
 }
 
+int launch_desc(const attn_mask_params&, int32_t, int32_t*, void*) { no_gpu(__func__); }
 int launch_index_dense(const Problem&, const int32_t*, void*, void*) { no_gpu(__func__); }
 int launch_index_sparse(const Problem&, const uint8_t*, void*, void*) { no_gpu(__func__); }
 int launch_fwd(const Problem&, const void*, const void*, const void*, void*, void*, float*, const int32_t*,

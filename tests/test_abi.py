@@ -199,3 +199,14 @@ def test_block_select_noalloc_rejects_beyond_static_array():
                                        None) == attn.ATTN_ERR_WORKSPACE
     assert L.attn_block_select_noalloc(ctypes.byref(prob), None, fake, fake, fake, fake,
                                        None) == attn.ATTN_ERR_INVALID_ARG
+
+
+def test_device_descriptor_validation_without_launch():
+    L = attn.lib()
+    p, keep = attn.mask_params(MaskSpec("causal_document", cu_seqlens=(0, 10, 20)))
+    fake = ctypes.c_void_p(256)
+    # a DOCUMENT kind without the device copy of cu_seqlens, and a null output: rejected first
+    assert L.attn_mask_desc_build_device(ctypes.byref(p), 20, None, fake, None) == attn.ATTN_ERR_INVALID_ARG
+    assert L.attn_mask_desc_build_device(ctypes.byref(p), 20, fake, None, None) == attn.ATTN_ERR_INVALID_ARG
+    # cu_seqlens not ending at T (validated on the host copy)
+    assert L.attn_mask_desc_build_device(ctypes.byref(p), 21, fake, fake, None) == attn.ATTN_ERR_INVALID_ARG
