@@ -55,6 +55,7 @@ struct BwdArgs {
     int T, Hq, Hk, G, BMq, lgBMq, nb, sblock;
     float c;       // scale * log2(e)
     float scale;
+    int rev_lists;  // bwd_kernel walks its query lists from their end
 };
 
 // Largest power of two s with bound * s <= 2^15 (1 when the bound is 0 or not finite).
@@ -325,10 +326,14 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
     int4 kd = {0, 0, 0, 0};
     if (!SPARSE && is_a && key_ok) kd = a.desc[my_key];
 
+    // The order of a key tile's query tiles is free. For the masks whose lists are suffixes
+    // (CAUSAL, PREFIX LM CAUSAL, SHARED QUESTION) the lists are walked from their end: the
+    // key tiles of a KV head that run together then stage the same query rows at about the
+    // same time, so the rows are read from L2 instead of once per key tile from memory.
     EntryStream es;           // list entries of the staged row loads (2 + PD steps ahead)
-    es.init(a.ent, lb, le - lb, lane);
+    es.init(a.ent, lb, le - lb, lane, a.rev_lists != 0);
     EntryStream esc;          // A: list entries of the steps whose P it forms
-    esc.init(a.ent, lb, le - lb, lane);
+    esc.init(a.ent, lb, le - lb, lane, a.rev_lists != 0);
 
     // Staging of this role's tensor (A: Q and LSE, B: dO and D). Rows past the end are
     // read from a valid row and get LSE = +inf (P = 0) and D = 0 when stored.
@@ -930,6 +935,8 @@ int launch_bwd_main(const Problem& P, const void* q, const void* k, const void* 
     a.sblock = P.sblock;
     a.c = P.scale * LOG2E;
     a.scale = P.scale;
+    a.rev_lists = !P.sparse && (P.kind == ATTN_MASK_CAUSAL || P.kind == ATTN_MASK_PREFIX_LM_CAUSAL ||
+                                P.kind == ATTN_MASK_SHARED_QUESTION);
     if (parts & BWD_PART_DKDV) {
         if (!P.sparse) {
             hipLaunchKernelGGL((bwd_kernel<4, false>), dim3(P.Hk * P.nkt_b), dim3(512), 0, s, a);

@@ -105,16 +105,18 @@ __device__ __forceinline__ u32x2 ds_read_tr16(const void* p) {
 // List entries of a work item, 64 per register: lane i of chunk register c holds entry
 // 64 c + i. Entries are read in non-decreasing order; the chunk after the current one is
 // loaded a whole chunk ahead and only touched (waited for) when the reader moves on to it.
+// With rev, get(j) returns the list's entry n - 1 - j (the list walked from its end).
 struct EntryStream {
     const int* ent;
-    int lb, n, chunk, cur, nxt;
+    int first, dir, n, chunk, cur, nxt;
     __device__ __forceinline__ int load(int c, int lane) const {
         const int j = 64 * c + lane;
-        return j < n ? ent[lb + j] : 0;
+        return j < n ? ent[first + dir * j] : 0;
     }
-    __device__ __forceinline__ void init(const int* e, int lb_, int n_, int lane) {
+    __device__ __forceinline__ void init(const int* e, int lb_, int n_, int lane, bool rev = false) {
         ent = e;
-        lb = lb_;
+        first = rev ? lb_ + n_ - 1 : lb_;
+        dir = rev ? -1 : 1;
         n = n_;
         chunk = 0;
         cur = load(0, lane);
