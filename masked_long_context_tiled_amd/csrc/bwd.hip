@@ -612,9 +612,10 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
     // Padded rows (fp16 per row): K is read as rows (S^T) and transposed (dQ^T), V as rows
     // only. Every operand read is a per-lane base plus a compile-time offset, which measured
     // faster than an XOR swizzle of 256-byte rows (whose lane-dependent addresses cost
-    // vector instructions), although K at this stride is not free of bank conflicts for both
-    // read patterns.
-    constexpr int KLD = HEAD_DIM + 16, VLD = HEAD_DIM + 8;
+    // vector instructions). No stride serves both of K's patterns at full rate: 152 keeps its
+    // row reads conflict-free and its transposed reads 2-way (160 would free the transposed
+    // reads and make the row reads 4-way); V's 136 is conflict-free for row reads.
+    constexpr int KLD = HEAD_DIM + 24, VLD = HEAD_DIM + 8;
     __shared__ __attribute__((aligned(16))) _Float16 Kh[2][FWD_BN * KLD];
     __shared__ __attribute__((aligned(16))) _Float16 Vh[2][FWD_BN * VLD];
     __shared__ int4 Ds[2][FWD_BN];

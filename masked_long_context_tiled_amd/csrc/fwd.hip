@@ -43,11 +43,15 @@ struct FwdArgs {
     float c;   // scale * log2(e)
 };
 
-// LDS row strides: K's 16-byte row reads and V's transposed reads (V is staged row-major
-// and V^T read with ds_read_b64_tr_b16, no transposing stores) are free of bank conflicts
-// at 136 and 144 bf16. Every MFMA's LDS operand is read three MFMAs ahead.
+// LDS row strides (16-bit elements). The MFMA operand patterns read at full LDS rate only
+// at some strides (measured, eight waves per CU): 16-byte row reads (lane l: row l % 32)
+// are conflict-free at 8 mod 16 (136, 152, ...; 2-way at 144, 4-way at 160), transposed
+// reads of a row-major tile (ds_read_b64_tr_b16: per 16 lanes 4 rows x 16 columns) at 160
+// and 224 (about 180 B/clk against 128 at 144..216). K is read as rows only, V (staged
+// row-major, V^T read transposed, no transposing stores) transposed only. Every MFMA's LDS
+// operand is read three MFMAs ahead.
 constexpr int K_LD = HEAD_DIM + 8;    // bf16 per K row in LDS
-constexpr int V_LD = HEAD_DIM + 16;   // bf16 per V row in LDS
+constexpr int V_LD = HEAD_DIM + 32;   // bf16 per V row in LDS
 
 // Block-sparse work items, four waves: at b = 128 one (query head, query block) row of the
 // keep matrix, each list entry a 128-key block walked as two 64-key tiles; at b = 64 (PAIR,
