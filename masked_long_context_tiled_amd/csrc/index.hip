@@ -36,6 +36,8 @@ __global__ void classify_kernel(const int4* __restrict__ desc, int T, ClassifyJo
     const int c0 = kt * j.BN, c1 = min(T, c0 + j.BN);
     const int rows = r1 - r0;
     bool any = false, all = true;
+    // unrolled so that several descriptor reads are in flight (the loop is latency-bound)
+#pragma unroll 8
     for (int c = c0; c < c1; ++c) {
         const int4 d = desc[c];
         const int n0 = max(0, min(d.y, r1) - max(d.x, r0));
@@ -159,6 +161,7 @@ __global__ void order_kernel(OrderJob a, OrderJob b) {
             cnt[c] = (j0 + c < n) ? j.ptr[j0 + c + 1] - j.ptr[j0 + c] : -1;
         __syncthreads();
         const int jn = min(1024, n - j0);
+#pragma unroll 8
         for (int c = 0; c < jn; ++c) {
             const int cj = cnt[c];
             rank += (cj > ci) || (cj == ci && j0 + c < i);
