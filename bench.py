@@ -216,7 +216,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the attention path runs on one GPU; --gpus {args.gpus} is not supported "
               "(the per-GPU share of a sharded run is the 1-GPU workload).", file=sys.stderr)
         sys.exit(2)
 

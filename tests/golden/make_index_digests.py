@@ -5,7 +5,7 @@ brute force over the materialised mask), the CSR / CSC lists of the non-empty ti
 their launch orders are reduced to SHA-256 digests of their canonical bytes, next to a
 few counts that make a mismatch readable. The GPU test builds the same index through the
 library and compares digests, so the full-size tile index is checked bit for bit without
-rebuilding 10^10-cell masks on the GPU machine.
+rebuilding 10^10-cell masks where the GPU tests run.
 
 Tile shapes are those of the kernels: forward tiles of 256 / G query positions x 64 keys,
 backward tiles of 256 / G query positions x 128 keys (G = Hq / Hk); the test also checks
