@@ -286,7 +286,14 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
     const bool is_a = w < NWK;
     const int kb = is_a ? w : w - NWK;
     const int rt = is_a ? tid : tid - NR;   // thread index within the role
-    const int g = blockIdx.x % a.Hk, y = blockIdx.x / a.Hk;
+    // Dense masks: KV head fastest, so consecutive workgroups go to different XCDs and every
+    // key tile of one KV head shares that XCD's L2 (which the reversed walk below exploits).
+    // Block-sparse: KV-head-major, so the whole chip works on one KV head's key blocks at a
+    // time and the random lists of all CUs draw on that head's fp16 Q and dO rows (256 MiB
+    // at 64K, within the 256 MB Infinity Cache) instead of eight heads' rows at once (one
+    // head per XCD, whose L2 serves few of them: the lists share no order).
+    const int g = SPARSE ? (int)blockIdx.x / a.nb : (int)blockIdx.x % a.Hk;
+    const int y = SPARSE ? (int)blockIdx.x % a.nb : (int)blockIdx.x / a.Hk;
     const int T = a.T;
 
     const OperandScales sc = operand_scales(a.stats);
