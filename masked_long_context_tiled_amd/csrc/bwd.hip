@@ -56,6 +56,8 @@ struct BwdArgs {
     float c;       // scale * log2(e)
     float scale;
     int rev_lists;  // bwd_kernel walks its query lists from their end
+    int splits;     // dense dK/dV: pieces per key tile (dkdv_splits)
+    float* part;    // splits > 1: partial dK [splits][T][Hk][128], then partial dV
 };
 
 // Largest power of two s with bound * s <= 2^15 (1 when the bound is 0 or not finite).
@@ -315,16 +317,20 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
     const float cS = a.c / (sQ * sK);       // exponent scale for the scaled scores
     const float inv_sV = 1.f / sV;
 
-    int key_base, col;
+    int key_base, col, piece = 0;
     if constexpr (!SPARSE) {
-        const int kt = a.order[y];
+        const int yy = y / a.splits;        // pieces of one key tile are consecutive items
+        piece = y - yy * a.splits;
+        const int kt = a.order[yy];
         key_base = kt * KEYS;
         col = kt;
     } else {
         key_base = y * a.sblock;
         col = g * a.nb + y;
     }
-    const int lb = a.ptr[col], le = a.ptr[col + 1];
+    // this item's piece of the key tile's list: entries [lb, le)
+    const int lb0 = a.ptr[col], n0 = a.ptr[col + 1] - lb0;
+    const int lb = lb0 + (int)((long)piece * n0 / a.splits), le = lb0 + (int)((long)(piece + 1) * n0 / a.splits);
     const int my_key = key_base + kb * 32 + l32;
     const bool key_ok = my_key < T;
     const size_t kv_row = (size_t)a.Hk * HEAD_DIM;
@@ -592,7 +598,11 @@ __global__ __launch_bounds__(NWK * 128) void bwd_kernel(BwdArgs a) {
 
     if (key_ok) {
         const float unscale = is_a ? 1.f / sO : a.scale / (sQ * sO);
-        float* outp = (is_a ? a.dv : a.dk) + (size_t)my_key * kv_row + (size_t)g * HEAD_DIM;
+        // split key tiles write their piece's partial sums, which dkdv_reduce_kernel adds up
+        float* dst = is_a ? a.dv : a.dk;
+        if (!SPARSE && a.splits > 1)
+            dst = a.part + ((size_t)(is_a ? a.splits : 0) + piece) * ((size_t)T * kv_row);
+        float* outp = dst + (size_t)my_key * kv_row + (size_t)g * HEAD_DIM;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -900,10 +910,26 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(BwdArgs a) {
     }
 }
 
+// dK and dV of split key tiles: the sum of the S partial results, in piece order (n4 = T * Hk *
+// 128 / 4 float4 per tensor; part holds dK's S pieces, then dV's).
+__global__ __launch_bounds__(256) void dkdv_reduce_kernel(const float4* __restrict__ part, float4* __restrict__ dk,
+                                                          float4* __restrict__ dv, size_t n4, int S) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (size_t)gridDim.x * blockDim.x) {
+        float4 a = part[i], b = part[(size_t)S * n4 + i];
+        for (int p = 1; p < S; ++p) {
+            const float4 x = part[(size_t)p * n4 + i], y = part[(size_t)(S + p) * n4 + i];
+            a.x += x.x; a.y += x.y; a.z += x.z; a.w += x.w;
+            b.x += y.x; b.y += y.y; b.z += y.z; b.w += y.w;
+        }
+        dk[i] = a;
+        dv[i] = b;
+    }
+}
+
 int launch_bwd_pre(const Problem& P, const void* q, const void* k, const void* v, const void* o,
                    const void* o_lo, const void* dout, float* dbuf, void* stream) {
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    const BwdLayout W = bwd_layout(P.Hq, P.Hk, P.T);
+    const BwdLayout W = bwd_layout(P.Hq, P.Hk, P.T, dkdv_splits(P));
     char* ws = reinterpret_cast<char*>(dbuf);
     float* stats = reinterpret_cast<float*>(ws + W.stats);
     hipLaunchKernelGGL(zero_stats_kernel, dim3(1), dim3(64), 0, s, stats);
@@ -933,7 +959,8 @@ int launch_bwd_main(const Problem& P, const void* q, const void* k, const void* 
     a.dout = static_cast<const bf16*>(dout);
     a.lse = lse;
     a.dbuf = dbuf;
-    const BwdLayout W = bwd_layout(P.Hq, P.Hk, P.T);
+    const int S = dkdv_splits(P);
+    const BwdLayout W = bwd_layout(P.Hq, P.Hk, P.T, S);
     const char* ws = reinterpret_cast<const char*>(dbuf);
     a.stats = reinterpret_cast<const float*>(ws + W.stats);
     a.qh = reinterpret_cast<const _Float16*>(ws + W.qh);
@@ -959,9 +986,17 @@ int launch_bwd_main(const Problem& P, const void* q, const void* k, const void* 
     a.scale = P.scale;
     a.rev_lists = !P.sparse && (P.kind == ATTN_MASK_CAUSAL || P.kind == ATTN_MASK_PREFIX_LM_CAUSAL ||
                                 P.kind == ATTN_MASK_SHARED_QUESTION);
+    a.splits = S;
+    a.part = S > 1 ? reinterpret_cast<float*>(const_cast<char*>(ws) + W.part) : nullptr;
     if (parts & BWD_PART_DKDV) {
         if (!P.sparse) {
-            hipLaunchKernelGGL((bwd_kernel<4, false>), dim3(P.Hk * P.nkt_b), dim3(512), 0, s, a);
+            hipLaunchKernelGGL((bwd_kernel<4, false>), dim3(P.Hk * P.nkt_b * S), dim3(512), 0, s, a);
+            if (S > 1) {
+                const size_t n4 = (size_t)P.T * P.Hk * HEAD_DIM / 4, nblk = (n4 + 255) / 256;
+                hipLaunchKernelGGL(dkdv_reduce_kernel, dim3((unsigned)(nblk < 2048 ? nblk : 2048)), dim3(256), 0, s,
+                                   reinterpret_cast<const float4*>(a.part), reinterpret_cast<float4*>(dk),
+                                   reinterpret_cast<float4*>(dv), n4, S);
+            }
         } else if (P.sblock == 64) {
             hipLaunchKernelGGL((bwd_kernel<2, true>), dim3(P.Hk * P.nb), dim3(256), 0, s, a);
         } else {

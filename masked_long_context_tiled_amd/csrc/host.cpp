@@ -355,7 +355,8 @@ attn_status attn_bwd_workspace_size(const attn_problem* prob, size_t* bytes_out)
     attn_status st = validate_problem(prob, &P);
     if (st != ATTN_OK) return st;
     if (!bytes_out) return ATTN_ERR_INVALID_ARG;
-    *bytes_out = bwd_layout(P.Hq, P.Hk, P.T).total;   // D, operand bounds, scaled fp16 Q, dO, K, V
+    // D, operand bounds, scaled fp16 Q, dO, K, V (and partial dK / dV for short sequences)
+    *bytes_out = bwd_layout(P.Hq, P.Hk, P.T, dkdv_splits(P)).total;
     return ATTN_OK;
 }
 

@@ -33,14 +33,27 @@ struct Problem {
     int nb;
 };
 
+// Pieces per key tile of the dense dK/dV pass. A short sequence has fewer key tiles (Hk * nkt_b
+// work items) than the chip runs at once, and the longest list then sets the time, so each
+// key tile's query list is cut into S consecutive pieces (S a power of two up to 8, the
+// smallest with Hk * nkt_b * S >= 512) whose partial dK / dV a reduction adds in a fixed
+// order. Block-sparse problems have enough work items and take S = 1.
+constexpr int dkdv_splits(const Problem& P) {
+    int S = 1;
+    if (!P.sparse)
+        while (S < 8 && (long)P.Hk * P.nkt_b * S < 512) S *= 2;
+    return S;
+}
+
 // Backward workspace, in order (each part 256-byte aligned):
 //   D [Hq][T] fp32 | BWD_STATS fp32 bounds of the operands | Q, dO [T][Hq][128] and
-//   K, V [T][Hk][128] as fp16 multiplied by their power-of-two scales.
+//   K, V [T][Hk][128] as fp16 multiplied by their power-of-two scales | with S > 1 dK/dV
+//   pieces, their partial dK [S][T][Hk][128] and dV [S][T][Hk][128] in fp32.
 constexpr int BWD_STATS = 4;
 struct BwdLayout {
-    size_t stats, qh, doh, kh, vh, total;
+    size_t stats, qh, doh, kh, vh, part, total;
 };
-constexpr BwdLayout bwd_layout(int Hq, int Hk, int T) {
+constexpr BwdLayout bwd_layout(int Hq, int Hk, int T, int S) {
     BwdLayout L{};
     const size_t qbytes = align256((size_t)T * Hq * 128 * 2), kbytes = align256((size_t)T * Hk * 128 * 2);
     L.stats = align256((size_t)Hq * T * 4);
@@ -48,7 +61,8 @@ constexpr BwdLayout bwd_layout(int Hq, int Hk, int T) {
     L.doh = L.qh + qbytes;
     L.kh = L.doh + qbytes;
     L.vh = L.kh + kbytes;
-    L.total = L.vh + kbytes;
+    L.part = L.vh + kbytes;
+    L.total = L.part + (S > 1 ? align256((size_t)2 * S * T * Hk * 128 * 4) : 0);
     return L;
 }
 
