@@ -213,6 +213,10 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run attn_cast_bf16 over 2^28 floats 5 times (reads 1 GiB, writes 512 MiB "
                          "per launch): the known-size kernel that scales the HBM byte counters")
+    ap.add_argument("--gemm-reference", action="store_true",
+                    help="only time torch.matmul (the ROCm BLAS library) on bf16 square matrices of 8192 and "
+                         "16384: the dense-GEMM rate this GPU reaches, as context for the attention kernels' "
+                         "fractions of the published MFMA peak; prints one JSON line")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -230,6 +234,30 @@ def main():
 
     if args.sweep:
         sweep(args, torch, dev)
+        return
+
+    if args.gemm_reference:
+        res = []
+        for n in (8192, 16384):
+            g = torch.Generator(device=dev).manual_seed(args.seed)
+            a_ = torch.randn(n, n, device=dev, dtype=torch.bfloat16, generator=g)
+            b_ = torch.randn(n, n, device=dev, dtype=torch.bfloat16, generator=g)
+            for _ in range(3):
+                c_ = a_ @ b_
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 20
+            e0.record()
+            for _ in range(reps):
+                c_ = a_ @ b_
+            e1.record()
+            e1.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            res.append({"n": n, "ms": round(ms, 4), "tflops": round(2 * n ** 3 / ms / 1e9, 1),
+                        "frac_peak": round(2 * n ** 3 / ms / 1e9 / PEAK_BF16_TFLOPS, 4)})
+            del a_, b_, c_
+        print(json.dumps({"gemm_reference": {"op": "torch.matmul bf16 (n x n) @ (n x n)", "points": res,
+                                             "peak_tflops": PEAK_BF16_TFLOPS}}))
         return
 
     if args.copy_calibration:
