@@ -362,8 +362,9 @@ attn_status attn_fwd(const attn_problem* prob, const void* q, const void* k, con
  *   o, o_lo   : the forward's outputs (o_lo may be NULL: D then uses the bf16 O alone)
  *   dq        : device fp32 [T][Hq][128], overwritten
  *   dk, dv    : device fp32 [T][Hk][128], overwritten
- *   ws        : workspace of attn_bwd_workspace_size bytes (D = rowsum(dO * O) and the
- *               operand bounds of the preprocess)
+ *   ws        : workspace of attn_bwd_workspace_size bytes (D = rowsum(dO * O), the operand
+ *               bounds and the scaled fp16 operand copies of the preprocess; on short
+ *               sequences also the partial dK / dV sums of split key tiles, see attn_bwd_main)
  * The three gradient products run on fp16 operands scaled by powers of two derived from
  * max |Q|, max |K|, max ||dO_i|| and max ||V_j|| (measured by the preprocess), which keeps
  * every operand in fp16 range; the scales are removed from the fp32 results.
@@ -388,21 +389,27 @@ attn_status attn_bwd_preprocess(const attn_problem* prob, const void* q, const v
  * dK = scale * dS^T Q (key-tile major, each key written once) and dQ = scale * dS K
  * (query-tile major, each row written once), with dS = P * (dO V^T - D). No atomics: the
  * gradients are deterministic. Requires attn_bwd_preprocess on the same ws first (stream
- * order).
+ * order). When the dense key tiles are too few to fill the GPU (Hk times the key tiles
+ * under 512, i.e. short sequences), each key tile's query list is cut into 2, 4 or 8
+ * pieces whose partial dK / dV sums go to the end of ws and are then added in a fixed
+ * order (still deterministic): ws is then written, so calls that share one ws must not
+ * overlap.
  */
 attn_status attn_bwd_main(const attn_problem* prob, const void* q, const void* k, const void* v,
                           const float* lse, const void* dout,
                           float* dq, float* dk, float* dv, const int32_t* desc_dev,
                           const void* index_dev, size_t index_bytes,
-                          const void* ws, size_t ws_bytes, void* stream);
+                          void* ws, size_t ws_bytes, void* stream);
 
 /* The two halves of attn_bwd_main, for callers that time or schedule them apart:
  * attn_bwd_dkdv writes dK and dV (key-tile major), attn_bwd_dq writes dQ (query-tile
- * major). Both read only the inputs, the forward's LSE and the preprocessed workspace. */
+ * major). Both read the inputs, the forward's LSE and the preprocessed workspace;
+ * attn_bwd_dq only reads ws, attn_bwd_dkdv also writes the partial sums of split key tiles
+ * into it on short sequences (as attn_bwd_main does). */
 attn_status attn_bwd_dkdv(const attn_problem* prob, const void* q, const void* k, const void* v,
                           const float* lse, const void* dout, float* dk, float* dv,
                           const int32_t* desc_dev, const void* index_dev, size_t index_bytes,
-                          const void* ws, size_t ws_bytes, void* stream);
+                          void* ws, size_t ws_bytes, void* stream);
 attn_status attn_bwd_dq(const attn_problem* prob, const void* q, const void* k, const void* v,
                         const float* lse, const void* dout, float* dq,
                         const int32_t* desc_dev, const void* index_dev, size_t index_bytes,

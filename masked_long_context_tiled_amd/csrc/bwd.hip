@@ -948,7 +948,7 @@ int launch_bwd_pre(const Problem& P, const void* q, const void* k, const void* v
 
 int launch_bwd_main(const Problem& P, const void* q, const void* k, const void* v, const float* lse,
                     const void* dout, float* dq, float* dk, float* dv, const int32_t* desc, const void* index,
-                    const float* dbuf, int parts, void* stream) {
+                    float* dbuf, int parts, void* stream) {
     const hipStream_t s = static_cast<hipStream_t>(stream);
     const IndexLayout L = index_layout(P);
     const char* base = static_cast<const char*>(index);
@@ -961,7 +961,7 @@ int launch_bwd_main(const Problem& P, const void* q, const void* k, const void* 
     a.dbuf = dbuf;
     const int S = dkdv_splits(P);
     const BwdLayout W = bwd_layout(P.Hq, P.Hk, P.T, S);
-    const char* ws = reinterpret_cast<const char*>(dbuf);
+    char* ws = reinterpret_cast<char*>(dbuf);
     a.stats = reinterpret_cast<const float*>(ws + W.stats);
     a.qh = reinterpret_cast<const _Float16*>(ws + W.qh);
     a.doh = reinterpret_cast<const _Float16*>(ws + W.doh);
@@ -987,7 +987,7 @@ int launch_bwd_main(const Problem& P, const void* q, const void* k, const void* 
     a.rev_lists = !P.sparse && (P.kind == ATTN_MASK_CAUSAL || P.kind == ATTN_MASK_PREFIX_LM_CAUSAL ||
                                 P.kind == ATTN_MASK_SHARED_QUESTION);
     a.splits = S;
-    a.part = S > 1 ? reinterpret_cast<float*>(const_cast<char*>(ws) + W.part) : nullptr;
+    a.part = S > 1 ? reinterpret_cast<float*>(ws + W.part) : nullptr;
     if (parts & BWD_PART_DKDV) {
         if (!P.sparse) {
             hipLaunchKernelGGL((bwd_kernel<4, false>), dim3(P.Hk * P.nkt_b * S), dim3(512), 0, s, a);

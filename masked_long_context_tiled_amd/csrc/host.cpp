@@ -394,7 +394,7 @@ attn_status attn_bwd_preprocess(const attn_problem* prob, const void* q, const v
 
 static attn_status bwd_parts(const attn_problem* prob, const void* q, const void* k, const void* v,
                              const float* lse, const void* dout, float* dq, float* dk, float* dv,
-                             const int32_t* desc_dev, const void* index_dev, size_t index_bytes, const void* ws,
+                             const int32_t* desc_dev, const void* index_dev, size_t index_bytes, void* ws,
                              size_t ws_bytes, void* stream, int parts) {
     Problem P;
     attn_status st = validate_problem(prob, &P);
@@ -405,12 +405,12 @@ static attn_status bwd_parts(const attn_problem* prob, const void* q, const void
     if (index_bytes < index_layout(P).total) return ATTN_ERR_WORKSPACE;
     if ((st = check_bwd_ws(prob, ws, ws_bytes)) != ATTN_OK) return st;
     return hip_status(launch_bwd_main(P, q, k, v, lse, dout, dq, dk, dv, desc_dev,
-                                      index_dev, (const float*)ws, parts, stream));
+                                      index_dev, (float*)ws, parts, stream));
 }
 
 attn_status attn_bwd_main(const attn_problem* prob, const void* q, const void* k, const void* v,
                           const float* lse, const void* dout, float* dq, float* dk, float* dv,
-                          const int32_t* desc_dev, const void* index_dev, size_t index_bytes, const void* ws,
+                          const int32_t* desc_dev, const void* index_dev, size_t index_bytes, void* ws,
                           size_t ws_bytes, void* stream) {
     return bwd_parts(prob, q, k, v, lse, dout, dq, dk, dv, desc_dev, index_dev, index_bytes, ws, ws_bytes, stream,
                      BWD_PART_DKDV | BWD_PART_DQ);
@@ -418,7 +418,7 @@ attn_status attn_bwd_main(const attn_problem* prob, const void* q, const void* k
 
 attn_status attn_bwd_dkdv(const attn_problem* prob, const void* q, const void* k, const void* v,
                           const float* lse, const void* dout, float* dk, float* dv, const int32_t* desc_dev,
-                          const void* index_dev, size_t index_bytes, const void* ws, size_t ws_bytes,
+                          const void* index_dev, size_t index_bytes, void* ws, size_t ws_bytes,
                           void* stream) {
     return bwd_parts(prob, q, k, v, lse, dout, nullptr, dk, dv, desc_dev, index_dev, index_bytes, ws, ws_bytes,
                      stream, BWD_PART_DKDV);
@@ -427,8 +427,9 @@ attn_status attn_bwd_dkdv(const attn_problem* prob, const void* q, const void* k
 attn_status attn_bwd_dq(const attn_problem* prob, const void* q, const void* k, const void* v,
                         const float* lse, const void* dout, float* dq, const int32_t* desc_dev,
                         const void* index_dev, size_t index_bytes, const void* ws, size_t ws_bytes, void* stream) {
-    return bwd_parts(prob, q, k, v, lse, dout, dq, nullptr, nullptr, desc_dev, index_dev, index_bytes, ws, ws_bytes,
-                     stream, BWD_PART_DQ);
+    // the dQ pass only reads the workspace
+    return bwd_parts(prob, q, k, v, lse, dout, dq, nullptr, nullptr, desc_dev, index_dev, index_bytes,
+                     const_cast<void*>(ws), ws_bytes, stream, BWD_PART_DQ);
 }
 
 attn_status attn_bwd(const attn_problem* prob, const void* q, const void* k, const void* v, const void* o,

@@ -96,7 +96,7 @@ int launch_bwd_pre(const Problem& P, const void* q, const void* k, const void* v
 enum { BWD_PART_DKDV = 1, BWD_PART_DQ = 2 };
 int launch_bwd_main(const Problem& P, const void* q, const void* k, const void* v, const float* lse,
                     const void* dout, float* dq, float* dk, float* dv, const int32_t* desc, const void* index,
-                    const float* dbuf, int parts, void* stream);
+                    float* dbuf, int parts, void* stream);
 int launch_cast_bf16(const float* in, void* out, size_t n, void* stream);
 int launch_block_select(const Problem& P, int mode, int topk, float topp, int keep_diag, const void* q,
                         const void* k, float* scores, uint8_t* keep, void* ws, void* stream);

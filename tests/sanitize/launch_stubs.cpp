@@ -23,7 +23,7 @@ int launch_fwd(const Problem&, const void*, const void*, const void*, void*, voi
 int launch_bwd_pre(const Problem&, const void*, const void*, const void*, const void*, const void*, const void*,
                    float*, void*) { no_gpu(__func__); }
 int launch_bwd_main(const Problem&, const void*, const void*, const void*, const float*, const void*, float*,
-                    float*, float*, const int32_t*, const void*, const float*, int, void*) { no_gpu(__func__); }
+                    float*, float*, const int32_t*, const void*, float*, int, void*) { no_gpu(__func__); }
 int launch_cast_bf16(const float*, void*, size_t, void*) { no_gpu(__func__); }
 int launch_block_select(const Problem&, int, int, float, int, const void*, const void*, float*, uint8_t*, void*,
                         void*) { no_gpu(__func__); }
