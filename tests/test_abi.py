@@ -210,3 +210,35 @@ def test_device_descriptor_validation_without_launch():
     assert L.attn_mask_desc_build_device(ctypes.byref(p), 20, fake, None, None) == attn.ATTN_ERR_INVALID_ARG
     # cu_seqlens not ending at T (validated on the host copy)
     assert L.attn_mask_desc_build_device(ctypes.byref(p), 21, fake, fake, None) == attn.ATTN_ERR_INVALID_ARG
+
+
+def _split_count(T, Hq, Hk):
+    """Pieces per dense dK/dV key tile the library chose, read off attn_bwd_workspace_size:
+    D [Hq][T] fp32, 256 bytes of bounds, fp16 Q and dO [T][Hq][128], fp16 K and V [T][Hk][128]
+    (each part 256-byte aligned), then with S > 1 pieces their fp32 partial dK and dV."""
+    a256 = lambda n: (n + 255) // 256 * 256
+    base = a256(Hq * T * 4) + 256 + 2 * a256(T * Hq * 128 * 2) + 2 * a256(T * Hk * 128 * 2)
+    extra = attn.bwd_workspace_size(attn.problem(T, Hq, Hk, "causal")) - base
+    if extra == 0:
+        return 1
+    per_piece = 2 * T * Hk * 128 * 4
+    S = extra // per_piece
+    assert extra == a256(S * per_piece), (extra, per_piece)
+    return S
+
+
+@pytest.mark.parametrize("T, Hq, Hk, S", [
+    (8192, 64, 8, 1),     # 8 KV heads x 64 key tiles of 128 = 512 work items: no split
+    (4096, 64, 8, 2),     # 256 -> 2 pieces
+    (2048, 64, 8, 4),     # 128 -> 4
+    (1024, 64, 8, 8),     # 64 -> 8 (the cap)
+    (512, 4, 1, 8),       # 4 -> capped at 8
+    (1024, 64, 64, 1),    # MHA: 64 x 8 = 512
+    (1024, 32, 32, 2),
+    (1000, 32, 16, 4),    # ragged: 8 key tiles of which the last is short
+])
+def test_dense_dkdv_split_count(T, Hq, Hk, S):
+    """Short sequences cut each dense key tile's query list into S pieces, the smallest power
+    of two up to 8 giving at least 512 dK/dV work items; the workspace grows by their
+    partial sums."""
+    assert _split_count(T, Hq, Hk) == S

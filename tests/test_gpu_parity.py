@@ -274,3 +274,16 @@ def test_repeat_runs_deterministic():
     b = run_gpu(T, Hq, Hk, spec, inputs=x)
     for k in ("o", "lse", "dq", "dk", "dv"):
         assert np.array_equal(a[k], b[k]), k
+
+
+@pytest.mark.parametrize("T, Hq, Hk, kind, S", [(1024, 32, 32, "causal", 2),
+                                                 (1000, 32, 16, "full_document", 4),
+                                                 (1024, 16, 8, "causal", 8)],
+                         ids=["pieces2", "pieces4", "pieces8"])
+def test_split_key_tiles(T, Hq, Hk, kind, S):
+    """Short sequences cut each dense dK/dV key tile's query list into S pieces whose partial
+    sums a reduction adds; every piece count the library picks (2, 4, 8) against the oracle,
+    element by element (the count itself is pinned on the CPU by test_abi)."""
+    spec = MaskSpec(kind) if kind == "causal" else MaskSpec(kind, cu_seqlens=document_cu_seqlens(11, T, 64, 400))
+    note(f"dK/dV split into {S} pieces per key tile")
+    _check(T, Hq, Hk, spec, seed=20 + S)
